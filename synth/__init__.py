@@ -1,0 +1,181 @@
+"""Seeded synthetic inputs for the offset-causal attention workloads.
+
+This module holds random draws and workload recipes only (shapes, seeds, cache
+lengths, planted keys).  It contains none of the attention arithmetic, so the
+oracle side and the GPU side can both read from it without sharing any of the
+method's code.
+
+Every tensor is drawn on the CPU as float32 N(0, 1) from its own
+``torch.Generator`` and then rounded to the run dtype (bf16 by round-to-nearest-even,
+or kept as f32).  Per-tensor seeds follow one base seed ``s``:
+
+    q = s, k = s+1, v = s+2, sink = s+3, cache lengths = s+4, planted keys = s+5.
+
+Workload shapes follow the pages' examples: head dim 16 with 8 query heads and
+2 KV heads over 40 tokens (sotaaz.com/post/attention-in-code, section 1 on
+MHA/MQA/GQA), a window of 8 (same page, section 2 on the ring buffer), and
+long-context prefill with an important key hidden inside a block of ordinary
+keys (patty.io review of RBS-Attention, section on mean dilution).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Optional
+
+import torch
+
+SEED_Q, SEED_K, SEED_V, SEED_SINK, SEED_LEN, SEED_OUTLIER = 0, 1, 2, 3, 4, 5
+
+
+def normal(shape, seed: int, dtype=torch.float32) -> torch.Tensor:
+    """float32 N(0,1) draw from a fresh generator seeded with ``seed``, cast to ``dtype``."""
+    g = torch.Generator().manual_seed(int(seed))
+    x = torch.randn(tuple(shape), generator=g, dtype=torch.float32)
+    return x if dtype == torch.float32 else x.to(dtype)
+
+
+@dataclass
+class Workload:
+    """One attention call's inputs.
+
+    q: [B, Hq, Tq, d]; k, v: [B, Hkv, Tk, d] where Tk is the number of cache rows
+    addressable per sequence.  ``cache_off`` (int32 [B]) gives each sequence's cache
+    offset; None means offset = Tk - Tq for every sequence.  ``window`` <= 0 means no
+    window.  ``sink`` is float32 [Hq] or None.  ``scale`` None means 1/sqrt(d).
+    """
+
+    name: str
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    cache_off: Optional[torch.Tensor] = None
+    window: int = 0
+    sink: Optional[torch.Tensor] = None
+    scale: Optional[float] = None
+    block_size: int = 0
+    keep_mean: float = 0.0
+    keep_radius: float = 0.0
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def shape(self):
+        B, Hq, Tq, d = self.q.shape
+        return dict(batch=B, n_heads=Hq, n_kv=self.k.shape[1], head_dim=d, tq=Tq, tk=self.k.shape[2])
+
+
+def attention_inputs(B, Hq, Hkv, Tq, Tk, d, dtype, seed=0, with_sink=False, window=0,
+                     cache_off=None, name="custom") -> Workload:
+    """Plain N(0,1) q/k/v (and optionally sink) with the standard per-tensor seeds."""
+    q = normal((B, Hq, Tq, d), seed + SEED_Q, dtype)
+    k = normal((B, Hkv, Tk, d), seed + SEED_K, dtype)
+    v = normal((B, Hkv, Tk, d), seed + SEED_V, dtype)
+    sink = normal((Hq,), seed + SEED_SINK) if with_sink else None
+    off = None if cache_off is None else torch.as_tensor(cache_off, dtype=torch.int32)
+    return Workload(name, q, k, v, cache_off=off, window=window, sink=sink)
+
+
+def tiny(seed=0, with_sink=False, window=0) -> Workload:
+    """Batch 1, 8 query heads, 2 KV heads, head dim 16, T = 40, float32."""
+    return attention_inputs(1, 8, 2, 40, 40, 16, torch.float32, seed, with_sink, window,
+                            name="tiny_f32_T40")
+
+
+def causal_prefill(T=8192, Hq=32, Hkv=8, d=128, seed=0) -> Workload:
+    """Causal prefill at cache offset 0, bf16, scale 1/sqrt(d)."""
+    w = attention_inputs(1, Hq, Hkv, T, T, d, torch.bfloat16, seed,
+                         name=f"causal_prefill_bf16_T{T}_{Hq}q{Hkv}kv_d{d}")
+    w.cache_off = torch.zeros(1, dtype=torch.int32)
+    w.scale = 1.0 / math.sqrt(d)
+    return w
+
+
+def window_sink_prefill(T=32768, W=1024, Hq=32, Hkv=8, d=128, seed=0) -> Workload:
+    """Sliding-window causal prefill with one N(0,1) sink logit per query head, bf16."""
+    w = attention_inputs(1, Hq, Hkv, T, T, d, torch.bfloat16, seed, with_sink=True, window=W,
+                         name=f"window_sink_prefill_bf16_T{T}_W{W}_{Hq}q{Hkv}kv_d{d}")
+    w.cache_off = torch.zeros(1, dtype=torch.int32)
+    return w
+
+
+def cache_lengths(B, lo, hi, seed=0) -> torch.Tensor:
+    """Per-sequence cached token counts, uniform integers in [lo, hi] inclusive."""
+    g = torch.Generator().manual_seed(seed + SEED_LEN)
+    return torch.randint(lo, hi + 1, (B,), generator=g, dtype=torch.int64).to(torch.int32)
+
+
+@dataclass
+class DecodeCache:
+    """A KV cache holding L_b tokens per sequence plus room for ``chunk`` new ones.
+
+    k, v: [B, Hkv, cap, d] with cap = max(L) + chunk; rows at or beyond L_b + chunk are
+    zero (never addressed).  q_decode: [B, Hq, 1, d] (the new token, whose K/V sit at row
+    L_b).  q_chunk: [B, Hq, chunk, d] (a chunk whose K/V sit at rows L_b .. L_b+chunk-1).
+    """
+
+    lengths: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    q_decode: torch.Tensor
+    q_chunk: torch.Tensor
+    chunk: int
+
+    def decode(self) -> Workload:
+        return Workload("decode", self.q_decode, self.k, self.v, cache_off=self.lengths.clone())
+
+    def prefill_chunk(self) -> Workload:
+        return Workload("chunk", self.q_chunk, self.k, self.v, cache_off=self.lengths.clone())
+
+
+def decode_cache(B=64, lo=1024, hi=32768, chunk=512, Hq=32, Hkv=8, d=128, seed=0,
+                 dtype=torch.bfloat16) -> DecodeCache:
+    """Cache lengths uniform in [lo, hi]; valid rows of k/v drawn N(0,1) sequence by sequence."""
+    L = cache_lengths(B, lo, hi, seed)
+    cap = int(L.max()) + chunk
+    k = torch.zeros((B, Hkv, cap, d), dtype=dtype)
+    v = torch.zeros((B, Hkv, cap, d), dtype=dtype)
+    gk = torch.Generator().manual_seed(seed + SEED_K)
+    gv = torch.Generator().manual_seed(seed + SEED_V)
+    for b in range(B):
+        n = int(L[b]) + chunk
+        k[b, :, :n] = torch.randn((Hkv, n, d), generator=gk).to(dtype)
+        v[b, :, :n] = torch.randn((Hkv, n, d), generator=gv).to(dtype)
+    q_dec = normal((B, Hq, 1, d), seed + SEED_Q, dtype)
+    q_chunk = normal((B, Hq, chunk, d), seed + SEED_Q + 100, dtype)
+    return DecodeCache(L, k, v, q_dec, q_chunk, chunk)
+
+
+def block_sparse_prefill(T=65536, BS=128, Hq=32, Hkv=8, d=128, frac=0.05, norm_mult=6.0,
+                         keep_mean=0.05, keep_radius=0.05, seed=0) -> Workload:
+    """Long causal prefill with planted outlier keys.
+
+    q, v ~ N(0,1).  k ~ N(0,1) except that, for every KV head, round(frac * nb) key blocks
+    (nb = T / BS, chosen without replacement) each get one key replaced: at a random slot
+    of the block, the key becomes ``norm_mult * sqrt(d)`` times the unit vector of the
+    mean of a random query block qb >= kb, the mean taken over the group's query heads and
+    the block's rows (bf16 values, computed in float64).  Planted positions are returned
+    in ``meta['planted']`` as (kv_head, key_block, slot, query_block) rows.
+    """
+    w = attention_inputs(1, Hq, Hkv, T, T, d, torch.bfloat16, seed,
+                         name=f"block_sparse_prefill_bf16_T{T}_BS{BS}_{Hq}q{Hkv}kv_d{d}")
+    w.cache_off = torch.zeros(1, dtype=torch.int32)
+    nb = T // BS
+    g_heads = Hq // Hkv
+    n_plant = int(math.floor(frac * nb + 0.5))
+    gen = torch.Generator().manual_seed(seed + SEED_OUTLIER)
+    planted = []
+    for kvh in range(Hkv):
+        blocks = torch.randperm(nb, generator=gen)[:n_plant].sort().values
+        for kb in blocks.tolist():
+            slot = int(torch.randint(0, BS, (1,), generator=gen))
+            qb = int(torch.randint(kb, nb, (1,), generator=gen))
+            rows = w.q[0, kvh * g_heads:(kvh + 1) * g_heads, qb * BS:(qb + 1) * BS, :]
+            mean = rows.to(torch.float64).reshape(-1, d).mean(0)
+            key = norm_mult * math.sqrt(d) * mean / mean.norm()
+            w.k[0, kvh, kb * BS + slot] = key.to(w.k.dtype)
+            planted.append((kvh, kb, slot, qb))
+    w.block_size = BS
+    w.keep_mean = keep_mean
+    w.keep_radius = keep_radius
+    w.meta["planted"] = planted
+    return w
