@@ -1,0 +1,188 @@
+/*
+ * soc_attn.h -- C ABI of the offset-causal attention library for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (all entry points)
+ * -----------------------------------
+ * Masked scaled-dot-product attention whose causal rule uses absolute positions
+ * (sotaaz.com/post/attention-in-code, section "the one function every design uses",
+ * functions attend and causal; the tilnote.io note on the Express framework, section
+ * "causal attention is a position problem"):
+ *
+ *   off_b  = cache offset of sequence b (tokens already cached before the query block)
+ *   Tk_b   = off_b + tq            (the block's own K/V rows are already in the cache)
+ *   pos(r) = off_b + r             absolute position of query row r, 0 <= r < tq
+ *   key j is visible to row r iff   j <= pos(r)
+ *                              and  (window <= 0  or  j > pos(r) - window)
+ *                              and  (no block list  or  key block j/bs is kept for
+ *                                    query block r/bs of this head)
+ *   s_j = scale * <q_r, k_j>;  o_r = sum_j e^{s_j} v_j / (sum_j e^{s_j} + [sink] e^{sink_h})
+ *   over visible j; a row with no visible key and no sink is 0.
+ *
+ * Grouped-query sharing (same page, section 1): query head h reads stored KV head
+ * h / (n_heads / n_kv); KV heads are never replicated.  The sink (same page, section 3)
+ * is one float32 logit per query head, in the same units as s_j (after the scale),
+ * that joins the softmax normaliser and has no value behind it.  The window keeps W
+ * keys including the query's own (factory.pai-world.com "Attention Variants", sliding
+ * window section, mask figure and build step 2).
+ *
+ * Layout and ownership
+ * --------------------
+ *  - Tensors are [batch, heads, tokens, head_dim] with head_dim contiguous; the other
+ *    three strides are given in ELEMENTS (attn_strides_t).  K and V share one stride set.
+ *  - q, k, v, o, sink, cache_off, block lists, masks, thresholds and workspaces are
+ *    DEVICE pointers owned by the caller.  The library never allocates or frees memory.
+ *  - bf16 path: head_dim = 128; every row start must be 16-byte aligned (pointers
+ *    16-byte aligned, strides multiples of 8 elements).  f32 path: head_dim in
+ *    {16, 32, 64, 128}, rows 16-byte aligned.
+ *  - Every call is asynchronous on the given stream; it returns once work is queued.
+ *  - Calls are re-entrant; the library keeps no mutable global state except a
+ *    thread-local error message and lazily read device properties.
+ *
+ * Errors
+ * ------
+ *  Non-zero returns are negative ATTN_E_* codes; attn_last_error() then returns a
+ *  thread-local message describing the failure.  Argument errors are detected before
+ *  any device work is queued.  Device-side preconditions (0 <= off_b, off_b + tq <= tk,
+ *  block-list indices in range) are the caller's; with the environment variable
+ *  ATTN_DEBUG=1 the library checks cache offsets on the host (one synchronous copy)
+ *  and synchronises after each launch to report launch failures.
+ */
+#ifndef SOC_ATTN_H
+#define SOC_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { ATTN_BF16 = 0, ATTN_F32 = 1 } attn_dtype_t;
+
+enum {
+  ATTN_OK = 0,
+  ATTN_E_INVAL = -1,       /* bad argument: null pointer, sizes, alignment, n_heads % n_kv != 0, tq > tk */
+  ATTN_E_UNSUPPORTED = -2, /* (dtype, head_dim, block_size, rows per KV group) combination not built */
+  ATTN_E_WORKSPACE = -3,   /* workspace missing or smaller than the matching *_workspace_bytes() */
+  ATTN_E_HIP = -4          /* the HIP runtime reported an error while queueing work */
+};
+
+/* Strides in elements of the batch, head and token axes (head_dim is contiguous). */
+typedef struct {
+  int64_t b, h, t;
+} attn_strides_t;
+
+/* tk = K/V rows addressable per sequence: the uniform key count when cache_off is NULL
+ * (then off_b = tk - tq for every b), otherwise the cache capacity. */
+typedef struct {
+  int32_t batch, n_heads, n_kv, head_dim, tq, tk;
+  attn_dtype_t dtype;
+} attn_shape_t;
+
+/*
+ * attn_prefill -- attention for a block of tq query rows per sequence (prefill, chunked
+ * prefill or decode) against the cache.
+ *
+ *  q          [batch, n_heads, tq, head_dim]   (dtype)
+ *  k, v       [batch, n_kv, tk, head_dim]      (dtype), strides kv_strides
+ *  o          [batch, n_heads, tq, head_dim]   output (dtype), written for every row
+ *  cache_off  device int32 [batch], or NULL (off_b = tk - tq)
+ *  window     <= 0: no window; W > 0 keeps keys pos-W < j <= pos.  Key tiles entirely
+ *             outside the window or beyond pos are never read.
+ *  sink       device float32 [n_heads] or NULL (a -inf entry behaves as no sink)
+ *  scale      <= 0 means 1/sqrt(head_dim)
+ *  block_list NULL for dense, or device int32 [batch, n_heads, nQB, 1 + nKB] with
+ *             nQB = ceil(tq / block_size), nKB = ceil(tk / block_size): entry 0 of each
+ *             (b, h, qb) row is the count n of kept key blocks, entries 1..n the kept key
+ *             block indices in ascending order (as written by attn_block_select).  Query
+ *             block qb covers rows [qb*bs, (qb+1)*bs) of the tq block; key block kb covers
+ *             absolute keys [kb*bs, (kb+1)*bs).  Unlisted key blocks are never read
+ *             (patty.io RBS-Attention review, section on regular block-sparse execution).
+ *  block_size ignored when block_list is NULL; bf16 path requires 128.
+ */
+int attn_prefill(const attn_shape_t* shape, const void* q, attn_strides_t q_strides, const void* k,
+                 const void* v, attn_strides_t kv_strides, void* o, attn_strides_t o_strides,
+                 const int32_t* cache_off, int32_t window, const float* sink, float scale,
+                 const int32_t* block_list, int32_t block_size, hipStream_t stream);
+
+/*
+ * attn_decode_workspace_bytes -- bytes of device workspace attn_decode needs for this
+ * shape and split size (split_tokens <= 0 selects the default split).  Returns 0 for
+ * an invalid shape.
+ */
+size_t attn_decode_workspace_bytes(const attn_shape_t* shape, int32_t split_tokens);
+
+/*
+ * attn_decode -- split-KV attention for a few query rows per sequence (decode steps or
+ * short speculative blocks).  Same arguments and semantics as attn_prefill without a
+ * block list.  The keys of each sequence are cut into splits of split_tokens; one pass
+ * computes an unnormalised partial (running max, sum, weighted V sum) per split and
+ * query row in float32 into the workspace, a second pass merges the partials with the
+ * sink (added exactly once per row) and writes o.  Each K/V element is read once per
+ * call: all n_heads / n_kv query heads of a group are served from one read.
+ *  bf16 path: (n_heads / n_kv) * tq <= 32.  f32 path: any tq.
+ *  workspace  device memory of at least attn_decode_workspace_bytes(shape, split_tokens)
+ *             bytes (256-byte aligned); its contents on entry do not matter.
+ */
+int attn_decode(const attn_shape_t* shape, const void* q, attn_strides_t q_strides, const void* k,
+                const void* v, attn_strides_t kv_strides, void* o, attn_strides_t o_strides,
+                const int32_t* cache_off, int32_t window, const float* sink, float scale,
+                void* workspace, size_t workspace_bytes, int32_t split_tokens, hipStream_t stream);
+
+/*
+ * attn_block_select_workspace_bytes -- device workspace for attn_block_select.
+ */
+size_t attn_block_select_workspace_bytes(const attn_shape_t* shape, int32_t block_size);
+
+/*
+ * attn_block_select -- block mask for block-sparse prefill: a mean-centroid score OR'd
+ * with a max-key-radius rescue score (patty.io review of RBS-Attention: sections on the
+ * centroid score, mean dilution, the radius signal and the two independently thresholded
+ * branches).  All arithmetic is float64 from exact bf16/f32 -> f64 conversion.
+ *
+ *  qmean[b,h,qb]   = mean of q rows [qb*bs, min((qb+1)*bs, tq))
+ *  c[b,kv,kb]      = mean of k rows [kb*bs, min((kb+1)*bs, Tk_b))
+ *  rad2[b,kv,kb]   = max over those rows of |k_j - c|^2
+ *  (qb, kb) admissible iff it holds at least one (row, key) pair the position/window
+ *  rule allows;  s1 = <qmean, c> on admissible pairs (unscaled).
+ *  Thresholds (order statistics, per prompt and head): with population size N and
+ *  n = floor(keep * N + 0.5), tau = the (n+1)-th largest value (-inf when n >= N).
+ *    tau_mean[b,h]    over the admissible s1 of (b, h)        (keep = keep_mean)
+ *    tau_radius[b,kv] over rad2 of the key blocks of (b, kv)  (keep = keep_radius)
+ *  mask[b,h,qb,kb] = admissible and (s1 > tau_mean[b,h] or rad2[b,h/g,kb] > tau_radius[b,h/g])
+ *
+ *  q [batch, n_heads, tq, d], k [batch, n_kv, tk, d] (dtype); cache_off as attn_prefill.
+ *  keep_mean, keep_radius  fractions in [0, 1]; a negative value means the matching
+ *             tau array is an INPUT (caller's absolute threshold) instead of an output.
+ *  tau_mean   device double [batch, n_heads];  tau_radius device double [batch, n_kv]
+ *  block_mask device uint8 [batch, n_heads, ceil(tq/bs), ceil(tk/bs)] output (0/1;
+ *             blocks at or beyond Tk_b are 0)
+ *  block_list device int32 [batch, n_heads, ceil(tq/bs), 1 + ceil(tk/bs)] output or NULL,
+ *             in the format attn_prefill reads.
+ *  workspace  at least attn_block_select_workspace_bytes(shape, block_size) bytes.
+ *  block_size >= 1 (the bf16 block-sparse prefill consumes block_size = 128).
+ */
+int attn_block_select(const attn_shape_t* shape, const void* q, attn_strides_t q_strides, const void* k,
+                      attn_strides_t k_strides, const int32_t* cache_off, int32_t window, int32_t block_size,
+                      double keep_mean, double keep_radius, double* tau_mean, double* tau_radius,
+                      uint8_t* block_mask, int32_t* block_list, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+/*
+ * attn_block_list_from_mask -- compact a caller-made block mask
+ * (device uint8 [rows, n_kb], nonzero = kept, rows = batch*n_heads*nQB) into the
+ * block-list format attn_prefill reads (device int32 [rows, 1 + n_kb]).
+ */
+int attn_block_list_from_mask(int64_t rows, int32_t n_kb, const uint8_t* block_mask, int32_t* block_list,
+                              hipStream_t stream);
+
+/* Thread-local description of the last non-zero return on this thread ("" if none). */
+const char* attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SOC_ATTN_H */

@@ -1,0 +1,22 @@
+"""Offset-causal attention for AMD Instinct MI355X (gfx950).
+
+The computation lives in hand-written HIP kernels behind the C ABI of
+``include/soc_attn.h`` (``libsoc_attn.so``); this package is the thin binding:
+
+    attn_prefill(q, k, v, cache_off=None, window=0, sink=None, scale=None, block_list=None)
+    attn_decode(q, k, v, cache_off=None, window=0, sink=None, scale=None, split_tokens=0)
+    attn_block_select(q, k, block_size=128, keep_mean=0.05, keep_radius=0.05, ...)
+    attn_block_list_from_mask(mask)
+
+PyTorch supplies device memory and the current stream only.  If the library has not
+been built, every call raises; there is no fallback path.
+"""
+from .api import (  # noqa: F401
+    AttnError,
+    attn_block_list_from_mask,
+    attn_block_select,
+    attn_block_select_workspace_bytes,
+    attn_decode,
+    attn_decode_workspace_bytes,
+    attn_prefill,
+)

@@ -1,0 +1,320 @@
+// C-ABI entry points: argument validation, variant selection, workspace carving, launches.
+// Every argument error is detected here, before any device work is queued.
+
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+#include "soc_attn.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+bool debug_mode() {
+  static const bool on = [] {
+    const char* e = std::getenv("ATTN_DEBUG");
+    return e && e[0] == '1';
+  }();
+  return on;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(ATTN_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t elem_size(attn_dtype_t t) { return t == ATTN_BF16 ? 2 : 4; }
+
+bool strides_ok(const attn_strides_t& s, size_t esz) {
+  const int64_t m = (int64_t)(16 / esz);
+  return s.b >= 0 && s.h >= 0 && s.t >= 0 && s.b % m == 0 && s.h % m == 0 && s.t % m == 0;
+}
+
+// Common shape checks.  Returns ATTN_OK or an error code (message set).
+int check_shape(const attn_shape_t* s) {
+  if (!s) return fail(ATTN_E_INVAL, "shape is NULL");
+  if (s->batch < 0 || s->n_heads < 1 || s->n_kv < 1 || s->head_dim < 1 || s->tq < 0 || s->tk < 0)
+    return fail(ATTN_E_INVAL, "shape has a negative or zero size");
+  if (s->n_heads % s->n_kv != 0) return fail(ATTN_E_INVAL, "n_heads must be a multiple of n_kv");
+  if (s->tq > s->tk) return fail(ATTN_E_INVAL, "tq > tk: the query block's keys must already be in the cache");
+  if (s->tk > (1 << 30)) return fail(ATTN_E_INVAL, "tk above 2^30 is not supported");
+  if (s->dtype != ATTN_BF16 && s->dtype != ATTN_F32) return fail(ATTN_E_UNSUPPORTED, "unknown dtype");
+  return ATTN_OK;
+}
+
+int check_attn_dtype(const attn_shape_t* s) {
+  if (s->dtype == ATTN_BF16 && s->head_dim != 128)
+    return fail(ATTN_E_UNSUPPORTED, "bf16 attention is built for head_dim 128 only");
+  if (s->dtype == ATTN_F32 && s->head_dim != 16 && s->head_dim != 32 && s->head_dim != 64 && s->head_dim != 128)
+    return fail(ATTN_E_UNSUPPORTED, "f32 attention supports head_dim 16, 32, 64 or 128");
+  return ATTN_OK;
+}
+
+int check_tensors(const attn_shape_t* s, const void* q, attn_strides_t qs, const void* k, const void* v,
+                  attn_strides_t kvs, const void* o, attn_strides_t os) {
+  if (!q || !k || !v || !o) return fail(ATTN_E_INVAL, "q, k, v and o must be non-NULL device pointers");
+  const size_t esz = elem_size(s->dtype);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(ATTN_E_INVAL, "q, k, v and o must be 16-byte aligned");
+  if (!strides_ok(qs, esz) || !strides_ok(kvs, esz) || !strides_ok(os, esz))
+    return fail(ATTN_E_INVAL, "strides must be non-negative multiples of 16 bytes (in elements)");
+  return ATTN_OK;
+}
+
+int check_offsets_debug(const attn_shape_t* s, const int32_t* cache_off, hipStream_t stream) {
+  if (!debug_mode() || !cache_off || s->batch == 0) return ATTN_OK;
+  std::vector<int32_t> h(s->batch);
+  hipError_t e = hipMemcpyAsync(h.data(), cache_off, sizeof(int32_t) * s->batch, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "ATTN_DEBUG: reading cache_off");
+  for (int b = 0; b < s->batch; ++b)
+    if (h[b] < 0 || (int64_t)h[b] + s->tq > s->tk)
+      return fail(ATTN_E_INVAL, "ATTN_DEBUG: cache_off[" + std::to_string(b) + "] = " + std::to_string(h[b]) +
+                                    " violates 0 <= off and off + tq <= tk");
+  return ATTN_OK;
+}
+
+int finish(hipError_t e, hipStream_t stream, const char* what) {
+  if (e != hipSuccess) return hip_fail(e, what);
+  if (debug_mode()) {
+    e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, what);
+  }
+  g_err.clear();
+  return ATTN_OK;
+}
+
+soc::AttnArgs make_args(const attn_shape_t* s, const void* q, attn_strides_t qs, const void* k, const void* v,
+                        attn_strides_t kvs, void* o, attn_strides_t os, const int32_t* cache_off, int32_t window,
+                        const float* sink, float scale) {
+  soc::AttnArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.q_sb = qs.b; a.q_sh = qs.h; a.q_st = qs.t;
+  a.kv_sb = kvs.b; a.kv_sh = kvs.h; a.kv_st = kvs.t;
+  a.o_sb = os.b; a.o_sh = os.h; a.o_st = os.t;
+  a.B = s->batch;
+  a.Hq = s->n_heads;
+  a.Hkv = s->n_kv;
+  a.g = s->n_heads / s->n_kv;
+  a.tq = s->tq;
+  a.tk = s->tk;
+  a.d = s->head_dim;
+  a.cache_off = cache_off;
+  a.window = window;
+  a.sink = sink;
+  const double sc = scale > 0.f ? (double)scale : 1.0 / std::sqrt((double)s->head_dim);
+  a.scale_log2 = (float)(sc * 1.4426950408889634);
+  return a;
+}
+
+int default_split(const attn_shape_t* s) {
+  int split = 1024;
+  while (split > 256 && (int64_t)s->batch * s->n_kv * ((s->tk + split - 1) / split) < 2048) split /= 2;
+  return split;
+}
+
+size_t round_up(size_t x, size_t m) { return (x + m - 1) / m * m; }
+
+struct SelectLayout {
+  int nqb, nkb;
+  size_t qmean, cT, rad2, score, total;  // byte offsets and total
+};
+
+SelectLayout select_layout(const attn_shape_t* s, int bs) {
+  SelectLayout L{};
+  L.nqb = (s->tq + bs - 1) / bs;
+  L.nkb = (s->tk + bs - 1) / bs;
+  const size_t d8 = sizeof(double);
+  size_t off = 0;
+  L.qmean = off;
+  off = round_up(off + d8 * s->batch * s->n_heads * L.nqb * s->head_dim, 256);
+  L.cT = off;
+  off = round_up(off + d8 * s->batch * s->n_kv * s->head_dim * L.nkb, 256);
+  L.rad2 = off;
+  off = round_up(off + d8 * s->batch * s->n_kv * L.nkb, 256);
+  L.score = off;
+  off = round_up(off + d8 * s->batch * s->n_heads * L.nqb * L.nkb, 256);
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_last_error(void) { return g_err.c_str(); }
+
+int attn_prefill(const attn_shape_t* shape, const void* q, attn_strides_t q_strides, const void* k, const void* v,
+                 attn_strides_t kv_strides, void* o, attn_strides_t o_strides, const int32_t* cache_off,
+                 int32_t window, const float* sink, float scale, const int32_t* block_list, int32_t block_size,
+                 hipStream_t stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if ((rc = check_attn_dtype(shape))) return rc;
+  if (shape->tq == 0 || shape->batch == 0) {
+    g_err.clear();
+    return ATTN_OK;
+  }
+  if ((rc = check_tensors(shape, q, q_strides, k, v, kv_strides, o, o_strides))) return rc;
+  if (block_list) {
+    if (block_size < 1) return fail(ATTN_E_INVAL, "block_size must be >= 1 with a block list");
+    if (shape->dtype == ATTN_BF16 && block_size != 128)
+      return fail(ATTN_E_UNSUPPORTED, "the bf16 block-sparse prefill needs block_size 128");
+  }
+  const int64_t nqt = (shape->tq + 127) / 128;
+  if (nqt * shape->batch * shape->n_heads >= (int64_t)1 << 31) return fail(ATTN_E_INVAL, "problem too large for one grid");
+  if ((rc = check_offsets_debug(shape, cache_off, stream))) return rc;
+
+  soc::AttnArgs a = make_args(shape, q, q_strides, k, v, kv_strides, o, o_strides, cache_off, window, sink, scale);
+  if (block_list) {
+    a.block_list = block_list;
+    a.block_size = block_size;
+    a.n_qb = (shape->tq + block_size - 1) / block_size;
+    a.list_stride = 1 + (shape->tk + block_size - 1) / block_size;
+  }
+  const hipError_t e = shape->dtype == ATTN_BF16 ? soc::launch_prefill_bf16(a, stream) : soc::launch_prefill_f32(a, stream);
+  return finish(e, stream, "attn_prefill launch");
+}
+
+size_t attn_decode_workspace_bytes(const attn_shape_t* shape, int32_t split_tokens) {
+  if (check_shape(shape) != ATTN_OK) return 0;
+  const int split = split_tokens > 0 ? split_tokens : default_split(shape);
+  const size_t nsplit = shape->tk > 0 ? (size_t)((shape->tk + split - 1) / split) : 1;
+  const size_t rows = (size_t)shape->batch * shape->n_heads * shape->tq;
+  return round_up(rows * nsplit * (shape->head_dim + 2) * sizeof(float), 256);
+}
+
+int attn_decode(const attn_shape_t* shape, const void* q, attn_strides_t q_strides, const void* k, const void* v,
+                attn_strides_t kv_strides, void* o, attn_strides_t o_strides, const int32_t* cache_off,
+                int32_t window, const float* sink, float scale, void* workspace, size_t workspace_bytes,
+                int32_t split_tokens, hipStream_t stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if ((rc = check_attn_dtype(shape))) return rc;
+  if (shape->tq == 0 || shape->batch == 0) {
+    g_err.clear();
+    return ATTN_OK;
+  }
+  if ((rc = check_tensors(shape, q, q_strides, k, v, kv_strides, o, o_strides))) return rc;
+  if (shape->dtype == ATTN_BF16 && (shape->n_heads / shape->n_kv) * shape->tq > 32)
+    return fail(ATTN_E_UNSUPPORTED, "bf16 decode serves at most 32 query rows per KV head ((n_heads/n_kv)*tq <= 32)");
+  const int split = split_tokens > 0 ? split_tokens : default_split(shape);
+  const int64_t nsplit = (shape->tk + split - 1) / split;
+  const size_t need = attn_decode_workspace_bytes(shape, split);
+  if (!workspace) return fail(ATTN_E_WORKSPACE, "workspace is NULL");
+  if (!aligned16(workspace)) return fail(ATTN_E_WORKSPACE, "workspace must be 16-byte aligned");
+  if (workspace_bytes < need)
+    return fail(ATTN_E_WORKSPACE, "workspace too small: need " + std::to_string(need) + " bytes");
+  if ((int64_t)shape->batch * shape->n_heads * shape->tq * nsplit >= (int64_t)1 << 31)
+    return fail(ATTN_E_INVAL, "problem too large for one grid");
+  if ((rc = check_offsets_debug(shape, cache_off, stream))) return rc;
+
+  soc::AttnArgs a = make_args(shape, q, q_strides, k, v, kv_strides, o, o_strides, cache_off, window, sink, scale);
+  a.part = static_cast<float*>(workspace);
+  a.nsplit = (int32_t)nsplit;
+  a.split = split;
+  hipError_t e = shape->dtype == ATTN_BF16 ? soc::launch_decode_bf16(a, stream) : soc::launch_decode_f32(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "attn_decode split launch");
+  e = soc::launch_decode_merge(a, shape->dtype == ATTN_BF16, stream);
+  return finish(e, stream, "attn_decode merge launch");
+}
+
+size_t attn_block_select_workspace_bytes(const attn_shape_t* shape, int32_t block_size) {
+  if (check_shape(shape) != ATTN_OK || block_size < 1) return 0;
+  return select_layout(shape, block_size).total;
+}
+
+int attn_block_select(const attn_shape_t* shape, const void* q, attn_strides_t q_strides, const void* k,
+                      attn_strides_t k_strides, const int32_t* cache_off, int32_t window, int32_t block_size,
+                      double keep_mean, double keep_radius, double* tau_mean, double* tau_radius,
+                      uint8_t* block_mask, int32_t* block_list, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (block_size < 1) return fail(ATTN_E_INVAL, "block_size must be >= 1");
+  const int d = shape->head_dim;
+  if (shape->dtype == ATTN_BF16 && d != 128 && d != 64)
+    return fail(ATTN_E_UNSUPPORTED, "bf16 block selection supports head_dim 64 or 128");
+  if (shape->dtype == ATTN_F32 && d != 16 && d != 32 && d != 64 && d != 128)
+    return fail(ATTN_E_UNSUPPORTED, "f32 block selection supports head_dim 16, 32, 64 or 128");
+  if (shape->tq == 0 || shape->batch == 0) {
+    g_err.clear();
+    return ATTN_OK;
+  }
+  if (!q || !k) return fail(ATTN_E_INVAL, "q and k must be non-NULL device pointers");
+  if (!tau_mean || !tau_radius || !block_mask)
+    return fail(ATTN_E_INVAL, "tau_mean, tau_radius and block_mask must be non-NULL device pointers");
+  const size_t esz = elem_size(shape->dtype);
+  if (!aligned16(q) || !aligned16(k)) return fail(ATTN_E_INVAL, "q and k must be 16-byte aligned");
+  if (!strides_ok(q_strides, esz) || !strides_ok(k_strides, esz))
+    return fail(ATTN_E_INVAL, "strides must be non-negative multiples of 16 bytes (in elements)");
+  if (std::isnan(keep_mean) || std::isnan(keep_radius)) return fail(ATTN_E_INVAL, "keep fractions must not be NaN");
+  const SelectLayout L = select_layout(shape, block_size);
+  if (!workspace) return fail(ATTN_E_WORKSPACE, "workspace is NULL");
+  if (!aligned16(workspace)) return fail(ATTN_E_WORKSPACE, "workspace must be 16-byte aligned");
+  if (workspace_bytes < L.total)
+    return fail(ATTN_E_WORKSPACE, "workspace too small: need " + std::to_string(L.total) + " bytes");
+  if ((int64_t)shape->batch * shape->n_heads * L.nqb >= (int64_t)1 << 31 ||
+      (int64_t)shape->batch * shape->n_kv * L.nkb >= (int64_t)1 << 31)
+    return fail(ATTN_E_INVAL, "problem too large for one grid");
+  if ((rc = check_offsets_debug(shape, cache_off, stream))) return rc;
+
+  soc::SelectArgs a{};
+  a.q = q;
+  a.k = k;
+  a.q_sb = q_strides.b; a.q_sh = q_strides.h; a.q_st = q_strides.t;
+  a.k_sb = k_strides.b; a.k_sh = k_strides.h; a.k_st = k_strides.t;
+  a.B = shape->batch;
+  a.Hq = shape->n_heads;
+  a.Hkv = shape->n_kv;
+  a.g = shape->n_heads / shape->n_kv;
+  a.tq = shape->tq;
+  a.tk = shape->tk;
+  a.d = d;
+  a.bs = block_size;
+  a.nqb = L.nqb;
+  a.nkb = L.nkb;
+  a.cache_off = cache_off;
+  a.window = window;
+  a.keep_mean = keep_mean;
+  a.keep_radius = keep_radius;
+  a.tau_mean = tau_mean;
+  a.tau_radius = tau_radius;
+  a.mask = block_mask;
+  a.list = block_list;
+  char* ws = static_cast<char*>(workspace);
+  a.qmean = reinterpret_cast<double*>(ws + L.qmean);
+  a.cT = reinterpret_cast<double*>(ws + L.cT);
+  a.rad2 = reinterpret_cast<double*>(ws + L.rad2);
+  a.score = reinterpret_cast<double*>(ws + L.score);
+  const hipError_t e = soc::launch_block_select(a, shape->dtype == ATTN_BF16, stream);
+  return finish(e, stream, "attn_block_select launch");
+}
+
+int attn_block_list_from_mask(int64_t rows, int32_t n_kb, const uint8_t* block_mask, int32_t* block_list,
+                              hipStream_t stream) {
+  if (rows < 0 || n_kb < 1) return fail(ATTN_E_INVAL, "rows must be >= 0 and n_kb >= 1");
+  if (rows == 0) {
+    g_err.clear();
+    return ATTN_OK;
+  }
+  if (!block_mask || !block_list) return fail(ATTN_E_INVAL, "block_mask and block_list must be non-NULL");
+  if (rows >= (int64_t)1 << 31) return fail(ATTN_E_INVAL, "too many rows for one grid");
+  return finish(soc::launch_list_from_mask(rows, n_kb, block_mask, block_list, stream), stream,
+                "attn_block_list_from_mask launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,68 @@
+// Internal declarations shared by the HIP kernels and the C-ABI dispatch layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace soc {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Arguments of one attention launch (prefill or decode).  Strides are in elements.
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  int64_t q_sb, q_sh, q_st;
+  int64_t kv_sb, kv_sh, kv_st;
+  int64_t o_sb, o_sh, o_st;
+  int32_t B, Hq, Hkv, g, tq, tk, d;
+  const int32_t* cache_off;  // device [B] or null (offset tk - tq)
+  int32_t window;            // <= 0: none
+  const float* sink;         // device [Hq] or null
+  float scale_log2;          // softmax scale * log2(e)
+  // block-sparse prefill
+  const int32_t* block_list;  // device [B, Hq, n_qb, list_stride] or null
+  int32_t block_size, n_qb, list_stride;
+  // split-KV decode
+  float* part;     // workspace: partial sums, [B*Hq*tq][nsplit][d] floats, then [..][nsplit][2]
+  int32_t nsplit;  // splits per sequence (capacity)
+  int32_t split;   // keys per split
+};
+
+// Decode workspace layout helpers (floats).
+__host__ __device__ inline size_t decode_rows(const AttnArgs& a) { return (size_t)a.B * a.Hq * a.tq; }
+__host__ __device__ inline size_t decode_o_floats(const AttnArgs& a) { return decode_rows(a) * a.nsplit * a.d; }
+__host__ __device__ inline size_t decode_ml_floats(const AttnArgs& a) { return decode_rows(a) * a.nsplit * 2; }
+
+struct SelectArgs {
+  const void* q;
+  const void* k;
+  int64_t q_sb, q_sh, q_st;
+  int64_t k_sb, k_sh, k_st;
+  int32_t B, Hq, Hkv, g, tq, tk, d, bs, nqb, nkb;  // nkb = ceil(tk / bs)
+  const int32_t* cache_off;
+  int32_t window;
+  double keep_mean, keep_radius;
+  double* tau_mean;    // [B, Hq]
+  double* tau_radius;  // [B, Hkv]
+  uint8_t* mask;       // [B, Hq, nqb, nkb]
+  int32_t* list;       // [B, Hq, nqb, 1 + nkb] or null
+  double* qmean;       // workspace [B, Hq, nqb, d]
+  double* cT;          // workspace [B, Hkv, d, nkb]
+  double* rad2;        // workspace [B, Hkv, nkb]
+  double* score;       // workspace [B, Hq, nqb, nkb]
+};
+
+hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t s);
+hipError_t launch_prefill_f32(const AttnArgs& a, hipStream_t s);
+hipError_t launch_decode_bf16(const AttnArgs& a, hipStream_t s);
+hipError_t launch_decode_f32(const AttnArgs& a, hipStream_t s);
+hipError_t launch_decode_merge(const AttnArgs& a, bool out_bf16, hipStream_t s);
+hipError_t launch_block_select(const SelectArgs& a, bool in_bf16, hipStream_t s);
+hipError_t launch_list_from_mask(int64_t rows, int32_t n_kb, const uint8_t* mask, int32_t* list,
+                                 hipStream_t s);
+
+}  // namespace soc

@@ -1,0 +1,200 @@
+"""GPU parity of attn_prefill / attn_decode against the float64 oracle (through the C ABI).
+
+Sizes span several 128-row query tiles and 64/128-key KV tiles with ragged tails,
+per-sequence cache offsets, windows, sinks and GQA/MQA/MHA groupings.  Bar: max-abs
+2e-2 for bf16 inputs, 1e-5 for the float32 path; invariants are checked bitwise.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import attend
+from sparse_offset_causal_amd import AttnError, attn_block_list_from_mask, attn_decode, attn_prefill
+from tests.gpu_helpers import BF16_TOL, F32_TOL, announce, dev, host64, max_abs, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def run_prefill(w, **kw):
+    return attn_prefill(dev(w.q), dev(w.k), dev(w.v), cache_off=dev(w.cache_off), window=w.window,
+                        sink=dev(w.sink), scale=w.scale, **kw)
+
+
+def oracle_of(w, **kw):
+    return attend(w.q, w.k, w.v, cache_off=w.cache_off, window=w.window, sink=w.sink, scale=w.scale, **kw)
+
+
+# ---------------------------------------------------------------- tiny float32 case
+@pytest.mark.parametrize("with_sink", [False, True])
+@pytest.mark.parametrize("window", [0, 8])
+def test_tiny_f32_prefill_and_token_by_token_decode(with_sink, window):
+    announce(f"tiny f32 sink={with_sink} window={window}")
+    w = synth.tiny(seed=0, with_sink=with_sink, window=window)
+    ref = oracle_of(w)
+    o = run_prefill(w)
+    assert max_abs(o, ref) <= F32_TOL
+    qd, kd, vd, sd = dev(w.q), dev(w.k), dev(w.v), dev(w.sink)
+    for split in (0, 8, 13):
+        worst = 0.0
+        for t in range(40):
+            off = torch.tensor([t], dtype=torch.int32, device="cuda")
+            step = attn_decode(qd[:, :, t:t + 1], kd, vd, cache_off=off, window=window, sink=sd, split_tokens=split)
+            worst = max(worst, max_abs(step[:, :, 0], ref[:, :, t]))
+            step_p = attn_prefill(qd[:, :, t:t + 1], kd, vd, cache_off=off, window=window, sink=sd)
+            worst = max(worst, max_abs(step_p[:, :, 0], ref[:, :, t]))
+        assert worst <= F32_TOL, (split, worst)
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_f32_other_head_dims(d):
+    w = synth.attention_inputs(2, 4, 2, 33, 70, d, torch.float32, seed=d, with_sink=True, window=20,
+                               cache_off=[37, 10])
+    assert max_abs(run_prefill(w), oracle_of(w)) <= F32_TOL
+    ref = attend(w.q[:, :, :3], w.k, w.v, cache_off=[37, 10], window=20, sink=w.sink)
+    o = attn_decode(dev(w.q[:, :, :3]), dev(w.k), dev(w.v), cache_off=dev(w.cache_off), window=20,
+                    sink=dev(w.sink), split_tokens=16)
+    assert max_abs(o, ref) <= F32_TOL
+
+
+# ---------------------------------------------------------------- bf16 prefill
+PREFILL_CASES = [
+    # B, Hq, Hkv, Tq, Tk, offsets, window, sink
+    (1, 8, 2, 300, 300, None, 0, False),
+    (2, 8, 2, 200, 700, None, 0, True),
+    (2, 4, 4, 129, 1000, [300, 871], 0, True),
+    (1, 8, 1, 640, 640, None, 200, True),
+    (1, 6, 2, 1, 777, None, 0, True),
+    (1, 8, 2, 64, 64, None, 1, False),
+    (3, 8, 8, 190, 450, [0, 100, 260], 77, True),
+    (1, 16, 8, 1024, 1536, None, 0, False),
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_CASES)
+def test_bf16_prefill_matches_oracle(case):
+    B, Hq, Hkv, Tq, Tk, offs, W, with_sink = case
+    announce(f"bf16 prefill {case}")
+    w = synth.attention_inputs(B, Hq, Hkv, Tq, Tk, 128, torch.bfloat16, seed=sum(case[:5]), with_sink=with_sink,
+                               window=W, cache_off=offs)
+    o = run_prefill(w)
+    err = max_abs(o, oracle_of(w))
+    assert err <= BF16_TOL, err
+
+
+def test_bf16_prefill_strided_views():
+    # q/k/v/o as views into larger buffers (head-major and token-major layouts)
+    base = synth.normal((1, 300, 12, 128), 5, torch.bfloat16)  # [B, T, H, d] layout
+    q = base[:, :, :8].permute(0, 2, 1, 3)
+    k = base[:, :, 8:10].permute(0, 2, 1, 3)
+    v = base[:, :, 10:12].permute(0, 2, 1, 3)
+    ref = attend(q, k, v, window=50)
+    out = torch.zeros((1, 300, 8, 128), dtype=torch.bfloat16, device="cuda").permute(0, 2, 1, 3)
+    attn_prefill(dev(base)[:, :, :8].permute(0, 2, 1, 3), dev(base)[:, :, 8:10].permute(0, 2, 1, 3),
+                 dev(base)[:, :, 10:12].permute(0, 2, 1, 3), window=50, out=out)
+    assert max_abs(out, ref) <= BF16_TOL
+
+
+def test_bf16_window_at_least_tk_is_bitwise_causal_and_sink_neg_inf_is_plain():
+    w = synth.attention_inputs(1, 8, 2, 333, 500, 128, torch.bfloat16, seed=3)
+    causal = run_prefill(w)
+    for W in (500, 501, 10 ** 6):
+        w.window = W
+        assert torch.equal(run_prefill(w), causal)
+    w.window = 0
+    w.sink = torch.full((8,), -math.inf)
+    assert torch.equal(run_prefill(w), causal)
+
+
+def test_bf16_masked_keys_never_matter_bitwise():
+    # Keys a row may not see (future keys of the block, keys before the window, and cache rows
+    # beyond Tk_b) are overwritten with large finite values: the output must not change at all.
+    B, Hq, Hkv, Tq, cap, W = 2, 8, 2, 200, 900, 150
+    offs = [400, 650]
+    w = synth.attention_inputs(B, Hq, Hkv, Tq, cap, 128, torch.bfloat16, seed=4, with_sink=True, window=W,
+                               cache_off=offs)
+    o1 = run_prefill(w)
+    k2, v2 = w.k.clone(), w.v.clone()
+    for b, off in enumerate(offs):
+        tkb = off + Tq
+        k2[b, :, tkb:] = 3e4
+        v2[b, :, tkb:] = -3e4
+        first_visible = off - W + 1  # smallest key any row of the block sees
+        k2[b, :, :first_visible] = 3e4
+        v2[b, :, :first_visible] = 3e4
+    w.k, w.v = k2, v2
+    o2 = run_prefill(w)
+    assert torch.equal(o1, o2)
+
+
+def test_bf16_deterministic_and_top_left_alignment_differs():
+    w = synth.attention_inputs(1, 8, 2, 256, 1024, 128, torch.bfloat16, seed=6)
+    o1, o2 = run_prefill(w), run_prefill(w)
+    assert torch.equal(o1, o2)
+    # block-internal causal masking (as if the block started at position 0) differs
+    top_left = attend(w.q, w.k[:, :, :256], w.v[:, :, :256])
+    assert max_abs(o1, top_left) > 0.1
+
+
+def test_bf16_block_list_all_kept_equals_dense_bitwise():
+    B, Hq, Hkv, Tq, Tk = 2, 8, 2, 384, 1000
+    w = synth.attention_inputs(B, Hq, Hkv, Tq, Tk, 128, torch.bfloat16, seed=7, with_sink=True, window=300,
+                               cache_off=[616, 200])
+    dense = run_prefill(w)
+    mask = torch.ones((B, Hq, 3, 8), dtype=torch.uint8, device="cuda")
+    lst = attn_block_list_from_mask(mask)
+    sparse = run_prefill(w, block_list=lst, block_size=128)
+    assert torch.equal(dense, sparse)
+
+
+def test_bf16_block_list_random_mask_matches_oracle():
+    B, Hq, Hkv, Tq, Tk = 2, 8, 2, 500, 900
+    w = synth.attention_inputs(B, Hq, Hkv, Tq, Tk, 128, torch.bfloat16, seed=8, with_sink=False, window=0,
+                               cache_off=[400, 100])
+    g = torch.Generator().manual_seed(9)
+    mask = (torch.rand((B, Hq, 4, 8), generator=g) < 0.4).to(torch.uint8)
+    mask[0, 0, 1] = 0  # an empty query block: its rows are 0
+    lst = attn_block_list_from_mask(mask.cuda())
+    o = run_prefill(w, block_list=lst, block_size=128)
+    ref = oracle_of(w, block_mask=mask.numpy(), block_size=128)
+    assert max_abs(o, ref) <= BF16_TOL
+    assert torch.count_nonzero(o[0, 0, 128:256]) == 0
+
+
+# ---------------------------------------------------------------- bf16 decode
+@pytest.mark.parametrize("tq", [1, 2, 8])
+@pytest.mark.parametrize("split", [0, 256, 1000])
+def test_bf16_decode_matches_oracle_and_prefill(tq, split):
+    announce(f"bf16 decode tq={tq} split={split}")
+    B, Hq, Hkv = 5, 32, 8
+    lengths = [1, 130, 1023, 2500, 4000]
+    cap = max(lengths) + tq
+    w = synth.attention_inputs(B, Hq, Hkv, tq, cap, 128, torch.bfloat16, seed=10 + tq, with_sink=True,
+                               cache_off=lengths)
+    ref = oracle_of(w)
+    o = attn_decode(dev(w.q), dev(w.k), dev(w.v), cache_off=dev(w.cache_off), sink=dev(w.sink), split_tokens=split)
+    assert max_abs(o, ref) <= BF16_TOL
+    assert max_abs(o, run_prefill(w)) <= BF16_TOL
+
+
+def test_bf16_decode_window_and_mqa():
+    B, Hq, Hkv, tq = 3, 8, 1, 4
+    lengths = [50, 700, 2049]
+    w = synth.attention_inputs(B, Hq, Hkv, tq, 2100, 128, torch.bfloat16, seed=21, with_sink=True, window=333,
+                               cache_off=lengths)
+    o = attn_decode(dev(w.q), dev(w.k), dev(w.v), cache_off=dev(w.cache_off), window=333, sink=dev(w.sink),
+                    split_tokens=128)
+    assert max_abs(o, oracle_of(w)) <= BF16_TOL
+
+
+def test_bf16_decode_rejects_too_many_rows():
+    w = synth.attention_inputs(1, 32, 4, 8, 64, 128, torch.bfloat16, seed=1)
+    with pytest.raises(AttnError, match="32 query rows"):
+        attn_decode(dev(w.q), dev(w.k), dev(w.v))
