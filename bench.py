@@ -1,0 +1,290 @@
+"""Benchmark: offset-causal attention on one MI355X.
+
+One step = one call of the hot path on one batch of synthetic input.  The headline
+``value`` is causal prefill throughput (TFLOP/s of algorithmic work) on the workload
+"batch 1, 32 query / 8 KV heads, head_dim 128, Tq = Tk = 8192, bf16".  The same JSON line
+also carries, under ``also``, the other workloads of the path measured the same way:
+sliding-window prefill with sinks (T = 32768, W = 1024), KV-cache decode (batch 64, cache
+lengths uniform in [1024, 32768]; decode KV-read GB/s), a 512-token chunk appended at each
+sequence's cache offset, and block-sparse prefill (T = 65536, block 128) with its block
+selection.
+
+Algorithmic work: prefill flops = 4 * head_dim * sum over heads of the allowed (row, key)
+pairs (QK^T and PV, 2 flops per multiply-add; masked halves of tiles and the softmax are not
+counted).  Decode bytes = K and V rows each sequence must read (2 * n_kv * Tk_b * d * 2 B)
+plus q and o.  Inputs are resident in HBM before timing starts.
+
+Timing: ``warmup`` untimed steps, then exactly ``steps`` steps between two device
+synchronisations; per-launch durations come from HIP events recorded on the stream the
+kernels run on.  ``cpu_baseline`` times the float64 oracle on the host on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+from sparse_offset_causal_amd import (attn_block_select, attn_decode, attn_decode_workspace_bytes,  # noqa: E402
+                                      attn_prefill)
+
+METRIC = "prefill TFLOP/s + decode KV-read GB/s, offset-causal GQA attention, 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
+
+
+# ------------------------------------------------------------------ algorithmic work
+def allowed_pairs(tq: int, tkb: int, window: int) -> int:
+    """(row, key) pairs the rule allows for one head: row r at pos = tkb - tq + r sees
+    keys max(0, pos - W + 1) .. pos."""
+    pos = np.arange(tkb - tq, tkb, dtype=np.int64)
+    lo = np.maximum(0, pos - window + 1) if window > 0 else np.zeros_like(pos)
+    return int((pos - lo + 1).sum())
+
+
+def prefill_flops(Hq, d, pairs_per_head_total):
+    return 4.0 * d * Hq * pairs_per_head_total
+
+
+def block_pairs(bs: int, qb: int, kb: int) -> int:
+    """Allowed pairs of a kept (query block, key block) at offset 0 without a window."""
+    if kb < qb:
+        return bs * bs
+    if kb == qb:
+        return bs * (bs + 1) // 2
+    return 0
+
+
+# ------------------------------------------------------------------ timing
+class Timer:
+    """Times `steps` calls of fn between synchronisations, with per-call HIP events."""
+
+    def __init__(self, fn, steps, warmup):
+        self.fn, self.steps, self.warmup = fn, steps, warmup
+
+    def run(self):
+        for _ in range(self.warmup):
+            self.fn()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(self.steps)]
+        t0 = time.perf_counter()
+        for s, e in ev:
+            s.record(stream)
+            self.fn()
+            e.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        per = [s.elapsed_time(e) for s, e in ev]  # ms
+        return dict(wall_s=wall, ms_per_step=wall * 1e3 / self.steps, launch_ms_mean=float(np.mean(per)),
+                    launch_ms_median=float(np.median(per)), launch_ms_min=float(np.min(per)))
+
+
+def to_dev(w):
+    f = lambda t: None if t is None else t.to("cuda", non_blocking=False)
+    return f(w.q), f(w.k), f(w.v), f(w.cache_off), f(w.sink)
+
+
+# ------------------------------------------------------------------ workloads
+def bench_causal_prefill(steps, warmup, T=8192):
+    w = synth.causal_prefill(T=T)
+    q, k, v, off, _ = to_dev(w)
+    out = torch.empty_like(q)
+    fn = lambda: attn_prefill(q, k, v, cache_off=off, scale=w.scale, out=out)
+    r = Timer(fn, steps, warmup).run()
+    flops = prefill_flops(32, 128, allowed_pairs(T, T, 0))
+    r.update(workload=w.name, flops_per_step=flops, value=flops / (r["ms_per_step"] * 1e-3) / 1e12,
+             kernel_tflops=flops / (r["launch_ms_mean"] * 1e-3) / 1e12, unit="TFLOP/s")
+    return r, w
+
+
+def bench_window_sink(steps, warmup, T=32768, W=1024):
+    w = synth.window_sink_prefill(T=T, W=W)
+    q, k, v, off, sink = to_dev(w)
+    out = torch.empty_like(q)
+    fn = lambda: attn_prefill(q, k, v, cache_off=off, window=W, sink=sink, out=out)
+    r = Timer(fn, steps, warmup).run()
+    flops = prefill_flops(32, 128, allowed_pairs(T, T, W))
+    r.update(workload=w.name, flops_per_step=flops, value=flops / (r["ms_per_step"] * 1e-3) / 1e12,
+             kernel_tflops=flops / (r["launch_ms_mean"] * 1e-3) / 1e12, unit="TFLOP/s")
+    return r
+
+
+def bench_decode_and_chunk(steps, warmup, B=64):
+    c = synth.decode_cache(B=B)
+    k, v = c.k.to("cuda"), c.v.to("cuda")
+    off = c.lengths.to("cuda")
+    L = c.lengths.numpy().astype(np.int64)
+    qd = c.q_decode.to("cuda")
+    od = torch.empty_like(qd)
+    ws = torch.empty(attn_decode_workspace_bytes(qd, k), dtype=torch.uint8, device="cuda")
+    fn = lambda: attn_decode(qd, k, v, cache_off=off, workspace=ws, out=od)
+    rd = Timer(fn, steps, warmup).run()
+    Hkv, d, Hq = 8, 128, 32
+    tk = L + 1
+    kv_bytes = float((2 * Hkv * tk * d * 2).sum())
+    qo_bytes = float(2 * B * Hq * d * 2)
+    nbytes = kv_bytes + qo_bytes
+    rd.update(workload=f"decode_bf16_B{B}_cache1024-32768_{Hq}q{Hkv}kv_d{d}", bytes_per_step=nbytes,
+              value=nbytes / (rd["ms_per_step"] * 1e-3) / 1e9, kernel_GBps=nbytes / (rd["launch_ms_mean"] * 1e-3) / 1e9,
+              unit="GB/s", mean_cache_len=float(L.mean()))
+    qc = c.q_chunk.to("cuda")
+    oc = torch.empty_like(qc)
+    fn = lambda: attn_prefill(qc, k, v, cache_off=off, out=oc)
+    rc = Timer(fn, max(3, steps // 4), max(1, warmup // 2)).run()
+    pairs = float(sum(allowed_pairs(c.chunk, int(l) + c.chunk, 0) for l in L))
+    flops = prefill_flops(Hq, d, pairs)
+    rc.update(workload=f"chunk512_bf16_B{B}_cache1024-32768_{Hq}q{Hkv}kv_d{d}", flops_per_step=flops,
+              value=flops / (rc["ms_per_step"] * 1e-3) / 1e12, kernel_tflops=flops / (rc["launch_ms_mean"] * 1e-3) / 1e12,
+              unit="TFLOP/s")
+    del k, v
+    return rd, rc
+
+
+def bench_block_sparse(steps, warmup, T=65536, BS=128):
+    w = synth.block_sparse_prefill(T=T, BS=BS)
+    q, k, v, _, _ = to_dev(w)
+    sel_fn = lambda: attn_block_select(q, k, block_size=BS, keep_mean=w.keep_mean, keep_radius=w.keep_radius)
+    rs = Timer(sel_fn, max(3, steps // 2), max(1, warmup // 2)).run()
+    sel = sel_fn()
+    out = torch.empty_like(q)
+    fn = lambda: attn_prefill(q, k, v, block_list=sel["list"], block_size=BS, out=out)
+    rp = Timer(fn, max(3, steps // 2), max(1, warmup // 2)).run()
+    m = sel["mask"].to(torch.int64)
+    nb = T // BS
+    diag = int(torch.diagonal(m, dim1=-2, dim2=-1).sum())
+    total = int(m.sum())
+    pairs = diag * block_pairs(BS, 0, 0) + (total - diag) * block_pairs(BS, 1, 0)
+    flops = 4.0 * 128 * pairs
+    adm = 32 * nb * (nb + 1) // 2
+    sel_bytes = float(q.numel() * 2 + k.numel() * 2)
+    rp.update(workload=f"block_sparse_prefill_bf16_T{T}_BS{BS}_32q8kv_d128", flops_per_step=flops,
+              value=flops / (rp["ms_per_step"] * 1e-3) / 1e12, kernel_tflops=flops / (rp["launch_ms_mean"] * 1e-3) / 1e12,
+              unit="TFLOP/s", kept_fraction=total / adm)
+    rs.update(workload=f"block_select_fp64_T{T}_BS{BS}_32q8kv_d128", bytes_per_step=sel_bytes,
+              value=sel_bytes / (rs["ms_per_step"] * 1e-3) / 1e9, unit="GB/s (q+k read)")
+    rp["select_plus_prefill_ms"] = rs["ms_per_step"] + rp["ms_per_step"]
+    return rs, rp
+
+
+# ------------------------------------------------------------------ CPU baseline
+def cpu_baseline(w, budget_s=15.0):
+    """The float64 oracle on host cores on a bounded sample of the causal-prefill workload:
+    whole heads (all 8192 rows) until the time budget is spent; value in TFLOP/s of the
+    same algorithmic flops."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import attend
+
+    T = w.q.shape[2]
+    heads_done, t0 = 0, time.perf_counter()
+    q, k, v = w.q.double().numpy(), w.k.double().numpy(), w.v.double().numpy()
+    for h in range(w.q.shape[1]):
+        attend(q, k, v, cache_off=[0], scale=w.scale, heads=[h])
+        heads_done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = 4.0 * 128 * heads_done * allowed_pairs(T, T, 0)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{heads_done} of 32 query heads, all {T} rows each (float64 numpy/BLAS), {dt:.1f} s"}
+
+
+# ------------------------------------------------------------------ main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", default="all", help="all | causal_prefill | window_sink | decode | block_sparse")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic", default=None, help="JSON file with measured HBM bytes per launch of the prefill kernel")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    torch.backends.cuda.matmul.allow_tf32 = False
+
+    def log(msg):
+        print(msg, file=sys.stderr, flush=True)
+
+    also = {}
+    head = None
+    w2 = None
+    if args.only in ("all", "causal_prefill"):
+        head, w2 = bench_causal_prefill(args.steps, args.warmup)
+        log(f"causal prefill: {head['value']:.1f} TFLOP/s ({head['ms_per_step']:.3f} ms/step)")
+    if args.only in ("all", "window_sink"):
+        r = bench_window_sink(args.steps, args.warmup)
+        also["window_sink_prefill"] = r
+        log(f"window+sink prefill: {r['value']:.1f} TFLOP/s ({r['ms_per_step']:.3f} ms)")
+        torch.cuda.empty_cache()
+    if args.only in ("all", "decode"):
+        rd, rc = bench_decode_and_chunk(args.steps, args.warmup)
+        also["decode"], also["chunk_prefill"] = rd, rc
+        log(f"decode: {rd['value']:.0f} GB/s ({rd['ms_per_step']:.3f} ms); chunk: {rc['value']:.1f} TFLOP/s")
+        torch.cuda.empty_cache()
+    if args.only in ("all", "block_sparse"):
+        rs, rp = bench_block_sparse(args.steps, args.warmup)
+        also["block_select"], also["block_sparse_prefill"] = rs, rp
+        log(f"block select: {rs['ms_per_step']:.3f} ms; block-sparse prefill {rp['value']:.1f} TFLOP/s "
+            f"({rp['ms_per_step']:.3f} ms, kept {rp['kept_fraction']:.3f})")
+        torch.cuda.empty_cache()
+
+    if head is None:  # a single non-headline workload was requested
+        name, r = next(iter(also.items()))
+        head = r
+    roof_bound = "hbm" if head["unit"] == "GB/s" else "mfma"
+    if roof_bound == "mfma":
+        achieved = head["flops_per_step"] / (head["launch_ms_mean"] * 1e-3) / 1e12
+        peak, unit = PEAK_BF16_TFLOPS, "TFLOP/s"
+    else:
+        achieved = head["bytes_per_step"] / (head["launch_ms_mean"] * 1e-3) / 1e9
+        peak, unit = PEAK_HBM_GBPS, "GB/s"
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            traffic = json.load(f).get(head["workload"])
+    line = {
+        "metric": METRIC,
+        "value": round(head["value"], 3),
+        "unit": head["unit"],
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1), cast to bf16; see synth/)",
+        "config": {"workload": head["workload"], "batch": 1, "n_heads": 32, "n_kv": 8, "head_dim": 128,
+                   "tq": 8192 if args.only in ("all", "causal_prefill") else None, "cache_offset": 0},
+        "roofline": {"bound": roof_bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+                     "frac": round(achieved / peak, 4), "traffic": traffic},
+        "also": {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv) for kk, vv in r.items()} for k, r in also.items()},
+    }
+    if not args.no_cpu_baseline and w2 is not None:
+        log("cpu baseline (float64 oracle) ...")
+        line["cpu_baseline"] = cpu_baseline(w2)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -80,7 +80,7 @@ def attend(q, k, v, cache_off=None, window=0, sink=None, scale=None, block_mask=
     Returns o [len(batches), len(heads), len(rows), d] float64, and with
     ``return_lse`` also lse = log sum_{allowed j} exp(s_j) (no sink; -inf if empty).
     """
-    q, k, v = _f64(q), _f64(k), _f64(v)
+    # inputs are widened to float64 slice by slice (exact), so a large cache is never copied whole
     B, Hq, Tq, d = q.shape
     Hkv, Tcap = k.shape[1], k.shape[2]
     if Hq % Hkv != 0:
@@ -105,12 +105,13 @@ def attend(q, k, v, cache_off=None, window=0, sink=None, scale=None, block_mask=
         jj = np.arange(tkb)
         for hi, h in enumerate(heads):
             kvh = h // g
-            K = k[b, kvh, :tkb]
-            V = v[b, kvh, :tkb]
+            K = _f64(k[b, kvh, :tkb])
+            V = _f64(v[b, kvh, :tkb])
+            Q = _f64(q[b, h])
             for r0 in range(0, len(rows), row_block):
                 r = rows[r0:r0 + row_block]
                 pos = int(off[b]) + r
-                s = scale * (q[b, h, r] @ K.T)
+                s = scale * (Q[r] @ K.T)
                 allow = key_allowed(pos[:, None], jj[None, :], window)
                 if bm is not None:
                     allow = allow & (bm[b, h][(r // block_size)[:, None], (jj // block_size)[None, :]] != 0)

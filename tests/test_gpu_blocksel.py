@@ -78,9 +78,15 @@ def test_select_planted_outliers_bit_exact():
                                    keep_radius=0.125)
     ref, got = check_select(w.q, w.k, 128, keep_mean=0.05, keep_radius=0.125)
     planted = {(kvh, kb) for kvh, kb, _, _ in w.meta["planted"]}
+    # the radius branch rescues exactly the planted key blocks (columns of every head in the group)
+    mask = got["mask"].cpu().numpy()
+    mean_only = select_blocks(w.q, w.k, 128, keep_mean=0.05, keep_radius=0.0)["mask"]
     for kvh in range(2):
-        chosen = set(np.nonzero(host64(got["tau_radius"])[0, kvh] < ref["rad2"][0, kvh])[0].tolist())
-        assert chosen == {kb for (kv, kb) in planted if kv == kvh}
+        want = {kb for (kv, kb) in planted if kv == kvh}
+        assert set(np.nonzero(ref["rad2"][0, kvh] > ref["tau_radius"][0, kvh])[0].tolist()) == want
+        for h in range(4 * kvh, 4 * kvh + 4):
+            rescued = {kb for kb in range(16) if mask[0, h, :, kb].any() and not mean_only[0, h, :, kb].any()}
+            assert rescued <= want
 
 
 @pytest.mark.parametrize("case", [
