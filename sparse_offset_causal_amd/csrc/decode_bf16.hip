@@ -6,13 +6,16 @@
 // serves all g = n_heads / n_kv query heads x tq rows of that group (<= 32 rows) from a
 // single read of the split's K and V: K/V bytes cross HBM exactly once per call.
 //
-// Per workgroup: 4 waves; the split is walked in 128-key tiles loaded cooperatively with
-// coalesced 16-byte loads (K row-major with an XOR chunk swizzle, V transposed) and
-// prefetched into registers one tile ahead; wave w takes keys 32w..32w+31 of each tile and
-// computes S^T = K Q^T and O^T += V^T P^T with v_mfma_f32_32x32x16_bf16 (query rows are the
-// MFMA's N columns, padded to 32).  The four waves' running (max, sum, O) are merged through
-// LDS at the end and the split's unnormalised partial is written in fp32.  The sink is not
-// applied here; the merge adds it exactly once per row.
+// A workgroup is one wave.  It streams its split in 32-key blocks through a private ring of
+// NST LDS stages (16 KB each: K then V, row-major with the same 16-byte-chunk XOR swizzles
+// as the prefill kernel) filled by HBM -> LDS DMA (global_load_lds_dwordx4), keeping
+// NST-1 blocks in flight while it consumes one; being alone in its workgroup, it only waits
+// on its own vector-memory counter, never on a barrier.  Per block it computes
+// S^T = K Q^T (query rows are the MFMA's N columns, padded to 32) and O^T += V^T P^T with
+// v_mfma_f32_32x32x16_bf16, V read transposed by ds_read_b64_tr_b16, with an online softmax
+// in the log2 domain (running max raised only when it grows by more than 2^8).  The split's
+// unnormalised partial (max, sum, O) is written in fp32.  The sink is not applied here;
+// the merge adds it exactly once per row.
 //
 // Merge: per (b, h, r) row, M = max(max_s m_s, sink), L = sum_s l_s 2^(m_s - M) + 2^(sink - M),
 // o = sum_s o_s 2^(m_s - M) / L (all in the log2 domain), rounded once to the output type.
@@ -24,21 +27,36 @@ namespace soc {
 namespace {
 
 constexpr int D = 128;
-constexpr int KT = 128;      // keys per tile
-constexpr int NTHR = 256;
-constexpr int VST = KT + 8;  // V^T row stride (elements)
-constexpr int LDS_BYTES = KT * D * 2 + D * VST * 2;  // 32 KB + 34 KB
+constexpr int KB = 32;                 // keys per block
+constexpr int NST = 4;                 // ring stages
+constexpr int HALF = KB * D;           // K (or V) elements of one stage
+constexpr int STAGE = 2 * HALF;        // 16 KB
+constexpr float RESCALE_SLACK = 8.0f;
 
-__device__ __forceinline__ int vt_col(int key) {
-  return (key & ~15) | (key & 3) | ((key & 4) << 1) | ((key & 8) >> 1);
+typedef short s16x4 __attribute__((__vector_size__(8)));
+typedef short s16x8 __attribute__((__vector_size__(16)));
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
+
+__device__ __forceinline__ int k_off(int row, int chunk) { return row * D + ((chunk ^ (row & 15)) << 3); }
+__device__ __forceinline__ int v_off(int row, int chunk) { return row * D + ((chunk ^ ((row & 3) << 2)) << 3); }
+
+// Wait until at most `blocks_after` blocks (16 DMA instructions each) are still in flight.
+__device__ __forceinline__ void wait_blocks(int blocks_after) {
+  if (blocks_after >= 3)
+    asm volatile("s_waitcnt vmcnt(48)" ::: "memory");
+  else if (blocks_after == 2)
+    asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
+  else if (blocks_after == 1)
+    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-__global__ void __launch_bounds__(NTHR) decode_split_bf16_d128(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
-  bf16_t* k_lds = (bf16_t*)lds;
-  bf16_t* vt_lds = (bf16_t*)(lds + KT * D * 2);
+__global__ void __launch_bounds__(64) decode_split_bf16_d128(AttnArgs a) {
+  __shared__ __attribute__((aligned(1024))) bf16_t lds[NST * STAGE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x;
   const int l32 = lane & 31, hh = lane >> 5;
   const int s = blockIdx.x % a.nsplit;
   const int rem = blockIdx.x / a.nsplit;
@@ -50,25 +68,43 @@ __global__ void __launch_bounds__(NTHR) decode_split_bf16_d128(AttnArgs a) {
   const int ks0 = s * a.split, ks1 = min(ks0 + a.split, tkb);
   const int kv_lo = a.window > 0 ? max(0, off - a.window + 1) : 0;
   const int kbeg = max(ks0, kv_lo), kend = ks1;
+  const int nblk = kbeg < kend ? (kend - kbeg + KB - 1) / KB : 0;
 
-  // query row of this lane: rho = head-in-group * tq + r
-  const int R = a.g * a.tq;
-  const int rho = l32;
-  const bool row_ok = rho < R;
-  const int h = kvh * a.g + (row_ok ? rho / a.tq : 0);
-  const int r = row_ok ? rho % a.tq : 0;
-  const int pos = row_ok ? off + r : -1;
-
-  const bf16_t* qp = (const bf16_t*)a.q + b * a.q_sb + h * a.q_sh + (int64_t)r * a.q_st;
   const bf16_t* kp = (const bf16_t*)a.k + b * a.kv_sb + kvh * a.kv_sh;
   const bf16_t* vp = (const bf16_t*)a.v + b * a.kv_sb + kvh * a.kv_sh;
 
+  auto issue = [&](int n) {
+    const int jb = kbeg + n * KB;
+    bf16_t* kdst = lds + (n % NST) * STAGE;
+    bf16_t* vdst = kdst + HALF;
+    const int sl = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 4 * i + (lane >> 4);
+      const int64_t rg = min(jb + r, kend - 1);
+      __builtin_amdgcn_global_load_lds((const void*)(kp + rg * a.kv_st + ((sl ^ (r & 15)) << 3)),
+                                       (lds_void_ptr)(kdst + i * 512), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vp + rg * a.kv_st + ((sl ^ ((r & 3) << 2)) << 3)),
+                                       (lds_void_ptr)(vdst + i * 512), 16, 0, 0);
+    }
+  };
+
+  // query row of this lane: rho = head-in-group * tq + r
+  const int R = a.g * a.tq;
+  const bool row_ok = l32 < R;
+  const int h = kvh * a.g + (row_ok ? l32 / a.tq : 0);
+  const int r = row_ok ? l32 % a.tq : 0;
+  const int pos = row_ok ? off + r : -1;
+  const bf16_t* qp = (const bf16_t*)a.q + b * a.q_sb + h * a.q_sh + (int64_t)r * a.q_st;
   bf16x8 qf[8];
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
     u32x4 z = {0u, 0u, 0u, 0u};
     qf[ks] = row_ok ? *(const bf16x8*)(qp + 16 * ks + 8 * hh) : as_bf16x8(z);
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  for (int n = 0; n < min(NST - 1, nblk); ++n) issue(n);
 
   f32x16 oacc[4];
 #pragma unroll
@@ -76,134 +112,83 @@ __global__ void __launch_bounds__(NTHR) decode_split_bf16_d128(AttnArgs a) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) oacc[tb][v] = 0.f;
   float m_run = SOC_NEG_INF, l_run = 0.f;
+  const float c = a.scale_log2;
+  const int trj = lane & 15;
+  const int tr_row = 4 * hh + (trj >> 2);
+  const int tr_col = ((lane >> 4) & 1) * 16 + 4 * (trj & 3);
 
-  u32x4 kreg[8], vreg[8];
-  auto load_tile = [&](int jb) {
+  for (int n = 0; n < nblk; ++n) {
+    if (n + NST - 1 < nblk) issue(n + NST - 1);
+    wait_blocks(min(NST - 1, nblk - 1 - n));
+    const bf16_t* kt = lds + (n % NST) * STAGE;
+    const bf16_t* vt = kt + HALF;
+    const int js = kbeg + n * KB;
+
+    f32x16 sacc;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int ci = tid + NTHR * i;
-      const int kk = ci >> 4, kc = ci & 15;
-      const int vk = ci & 127, vc = ci >> 7;
-      u32x4 z = {0u, 0u, 0u, 0u};
-      kreg[i] = (jb + kk < kend) ? *(const u32x4*)(kp + (int64_t)(jb + kk) * a.kv_st + kc * 8) : z;
-      vreg[i] = (jb + vk < kend) ? *(const u32x4*)(vp + (int64_t)(jb + vk) * a.kv_st + vc * 8) : z;
+    for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      sacc = mfma32x32x16(*(const bf16x8*)(kt + k_off(l32, 2 * ks + hh)), qf[ks], sacc);
+    float mx = SOC_NEG_INF;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int j = js + 8 * (v >> 2) + 4 * hh + (v & 3);
+      const bool ok = j < kend && j <= pos && (a.window <= 0 || j > pos - a.window);
+      sacc[v] = ok ? sacc[v] : SOC_NEG_INF;
+      mx = fmaxf(mx, sacc[v]);
     }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int ci = tid + NTHR * i;
-      const int kk = ci >> 4, kc = ci & 15;
-      *(u32x4*)(k_lds + kk * D + ((kc ^ (kk & 15)) << 3)) = kreg[i];
-      const int vk = ci & 127, vc = ci >> 7;
-      const int col = vt_col(vk);
-      const u32x4 w = vreg[i];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vt_lds[(vc * 8 + 2 * e) * VST + col] = __builtin_bit_cast(bf16_t, (uint16_t)(w[e] & 0xffffu));
-        vt_lds[(vc * 8 + 2 * e + 1) * VST + col] = __builtin_bit_cast(bf16_t, (uint16_t)(w[e] >> 16));
-      }
-    }
-  };
-
-  if (kbeg < kend) load_tile(kbeg);
-  for (int jb = kbeg; jb < kend; jb += KT) {
-    store_tile();
-    __syncthreads();
-    if (jb + KT < kend) load_tile(jb + KT);
-
-    const int js = jb + 32 * wave;  // this wave's 32 keys
-    if (js < kend) {
-      f32x16 sacc;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
-      const int krow = 32 * wave + l32;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 ka = *(const bf16x8*)(k_lds + krow * D + (((2 * ks + hh) ^ (krow & 15)) << 3));
-        sacc = mfma32x32x16(ka, qf[ks], sacc);
-      }
-      float x[16];
-      float mx = SOC_NEG_INF;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int j = js + 8 * (v >> 2) + 4 * hh + (v & 3);
-        const bool ok = j < kend && j <= pos && (a.window <= 0 || j > pos - a.window);
-        x[v] = ok ? sacc[v] * a.scale_log2 : SOC_NEG_INF;
-        mx = fmaxf(mx, x[v]);
-      }
-      mx = fmaxf(mx, swap_halves(mx));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = (m_new == SOC_NEG_INF) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      float lsum = 0.f;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        x[v] = fast_exp2(x[v] - m_use);
-        lsum += x[v];
-      }
-      l_run = l_run * alpha + lsum;
-      m_run = m_new;
+    mx = fmaxf(mx, swap_halves(mx));
+    const float m_cand = mx * c;
+    const bool upd = m_cand > m_run + RESCALE_SLACK;
+    if (__builtin_amdgcn_ballot_w64(upd) != 0) {
+      const float m_new = upd ? m_cand : m_run;
+      const float alpha = upd ? fast_exp2(m_run - m_new) : 1.f;
+      l_run *= alpha;
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) oacc[tb][v] *= alpha;
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        bf16x8 pb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pb[e] = (bf16_t)x[kk * 8 + e];
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-          const bf16x8 va = *(const bf16x8*)(vt_lds + (tb * 32 + l32) * VST + 32 * wave + 16 * kk + 8 * hh);
-          oacc[tb] = mfma32x32x16(va, pb, oacc[tb]);
-        }
-      }
+      m_run = m_new;
     }
-    __syncthreads();
+    const float nm = (m_run == SOC_NEG_INF) ? 0.f : -m_run;
+    bf16x8 pb[2];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const float p = fast_exp2(fmaf(sacc[v], c, nm));
+      l_run += p;
+      pb[v >> 3][v & 7] = (bf16_t)p;
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        const int row = 16 * kk + tr_row;
+        const int col = tb * 32 + tr_col;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vt + v_off(row, col >> 3) + (col & 7)));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vt + v_off(row + 8, col >> 3) + (col & 7)));
+        const s16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        oacc[tb] = mfma32x32x16(__builtin_bit_cast(bf16x8, va), pb[kk], oacc[tb]);
+      }
+    asm volatile("" ::: "memory");  // this stage's LDS reads stay ahead of its next refill
   }
 
-  // Merge the four waves' states through LDS (the tile buffers are free now).
-  float* lo = (float*)lds;               // [wave][tb][v][lane]
-  float* lml = lo + 4 * 4 * 16 * 64;     // [wave][lane][2]
-#pragma unroll
-  for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) lo[((wave * 4 + tb) * 16 + v) * 64 + lane] = oacc[tb][v];
-  lml[(wave * 64 + lane) * 2 + 0] = m_run;
-  lml[(wave * 64 + lane) * 2 + 1] = l_run;
-  __syncthreads();
-
-  float M = SOC_NEG_INF;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) M = fmaxf(M, lml[(w * 64 + lane) * 2]);
-  const float M_use = (M == SOC_NEG_INF) ? 0.f : M;
-  float wt[4], L = 0.f;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    wt[w] = fast_exp2(lml[(w * 64 + lane) * 2] - M_use);
-    L += (lml[(w * 64 + lane) * 2 + 1] + lml[(w * 64 + (lane ^ 32)) * 2 + 1]) * wt[w];
-  }
+  const float L = l_run + swap_halves(l_run);
   if (row_ok) {
     const int64_t rowid = ((int64_t)b * a.Hq + h) * a.tq + r;
     float* po = a.part + (rowid * a.nsplit + s) * D;
-    const int tb = wave;
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      f32x4 out;
+    for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int v = 4 * g4 + e;
-        float acc = 0.f;
+      for (int g4 = 0; g4 < 4; ++g4) {
+        f32x4 out;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) acc += lo[((w * 4 + tb) * 16 + v) * 64 + lane] * wt[w];
-        out[e] = acc;
+        for (int e = 0; e < 4; ++e) out[e] = oacc[tb][4 * g4 + e];
+        *(f32x4*)(po + tb * 32 + 8 * g4 + 4 * hh) = out;
       }
-      *(f32x4*)(po + tb * 32 + 8 * g4 + 4 * hh) = out;
-    }
-    if (wave == 0 && hh == 0) {
+    if (hh == 0) {
       float* pml = a.part + decode_o_floats(a) + (rowid * a.nsplit + s) * 2;
-      pml[0] = M;
+      pml[0] = m_run;
       pml[1] = L;
     }
   }
@@ -241,7 +226,7 @@ __global__ void __launch_bounds__(64) decode_merge(AttnArgs a) {
 hipError_t launch_decode_bf16(const AttnArgs& a, hipStream_t s) {
   const int64_t grid = (int64_t)a.B * a.Hkv * a.nsplit;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(decode_split_bf16_d128, dim3((unsigned)grid), dim3(NTHR), 0, s, a);
+  hipLaunchKernelGGL(decode_split_bf16_d128, dim3((unsigned)grid), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 

@@ -16,14 +16,21 @@
 //   need one exchange between the two wave halves, and the output O^T = V^T P^T again
 //   leaves one row per lane, so the softmax rescale is a per-lane scalar.
 //   Masks are computed from indices only on tiles that cross a row's causal limit or
-//   window edge.  The online softmax runs in the log2 domain in fp32; P is rounded to bf16
+//   window edge.  The online softmax runs in the log2 domain in fp32 with the scale folded
+//   into the exponent's FMA; the running max is only raised (and O, l rescaled) when a
+//   row's max grows by more than 2^8, so most tiles skip the rescale; P is rounded to bf16
 //   for the second MFMA; O accumulates in fp32 and is rounded to bf16 once at the end.
 //
-// LDS (34 KB): the K tile row-major with a 16-byte-chunk XOR swizzle (conflict-free 16-byte
-// reads of 16 consecutive keys), and the V tile transposed (V^T, 128 x 64 plus 8 pad) with
-// the key order inside each 16-key group permuted so that a lane's 8 contraction values are
-// one 16-byte read.  The next tile is prefetched into registers while the current one is
-// being consumed.
+// Memory path
+//   K and V tiles go HBM -> LDS directly (global_load_lds_dwordx4, 1 KB per wave
+//   instruction, no register staging) into a double buffer: the loads of tile n+1 are in
+//   flight while tile n is consumed, with one barrier per tile.  Both tiles are row-major
+//   with a 16-byte-chunk XOR swizzle applied on the load side.  K is read as the MFMA A
+//   operand with ds_read_b128 (chunk' = chunk ^ (row & 15): 16 consecutive keys hit 16
+//   distinct bank groups).  V is read already transposed with ds_read_b64_tr_b16 (each
+//   16-lane group reads a 4-key x 16-column block; chunk' = chunk ^ 4*(row & 3) makes the
+//   two groups of a half-wave cover all 64 banks once).  Rows past the last visible key
+//   are clamped to a valid row: their scores are masked, their probabilities are exactly 0.
 //
 // Grid order: workgroup i runs on XCD i % 8.  When the number of KV groups (batch x n_kv)
 // is a multiple of 8, each XCD is given whole KV groups (their K/V stay in that XCD's L2),
@@ -36,16 +43,17 @@ namespace soc {
 namespace {
 
 constexpr int D = 128;
-constexpr int QT = 128;       // query rows per workgroup
-constexpr int KT = 64;        // keys per tile
+constexpr int QT = 128;  // query rows per workgroup
+constexpr int KT = 64;   // keys per tile
 constexpr int NTHR = 256;
-constexpr int VST = KT + 8;   // V^T row stride (elements): 144 bytes
+constexpr int TILE_ELEMS = KT * D;              // one K or V tile, 16 KB
+constexpr int BUF_ELEMS = 2 * TILE_ELEMS;       // K then V
+constexpr float RESCALE_SLACK = 8.0f;           // log2 units the running max may lag
 
-// Column of key `key` (0..63) inside a V^T row: bits 2 and 3 swapped, so that the keys
-// {4h..4h+3, 8+4h..8+4h+3} of each 16-key group are contiguous at 8h.
-__device__ __forceinline__ int vt_col(int key) {
-  return (key & ~15) | (key & 3) | ((key & 4) << 1) | ((key & 8) >> 1);
-}
+typedef short s16x4 __attribute__((__vector_size__(8)));
+typedef short s16x8 __attribute__((__vector_size__(16)));
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
 
 __device__ __forceinline__ void map_block(int bid, const AttnArgs& a, int n_qt, int& qt, int& h, int& b) {
   const int units = a.B * a.Hkv;
@@ -71,12 +79,19 @@ __device__ __forceinline__ void map_block(int bid, const AttnArgs& a, int n_qt, 
   }
 }
 
-template <bool SPARSE>
-__global__ void __launch_bounds__(NTHR) prefill_bf16_d128(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16_t k_lds[KT * D];
-  __shared__ __attribute__((aligned(16))) bf16_t vt_lds[D * VST];
+// Element offset of (row, 16-byte chunk) inside a K / V tile.
+__device__ __forceinline__ int k_off(int row, int chunk) { return row * D + ((chunk ^ (row & 15)) << 3); }
+__device__ __forceinline__ int v_off(int row, int chunk) { return row * D + ((chunk ^ ((row & 3) << 2)) << 3); }
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+template <bool SPARSE>
+__global__ void __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2)))
+prefill_bf16_d128(AttnArgs a) {
+  __shared__ __attribute__((aligned(1024))) bf16_t lds[2 * BUF_ELEMS];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
   const int n_qt = (a.tq + QT - 1) / QT;
   int qt, h, b;
@@ -101,6 +116,43 @@ __global__ void __launch_bounds__(NTHR) prefill_bf16_d128(AttnArgs a) {
   const bf16_t* kp = (const bf16_t*)a.k + b * a.kv_sb + kvh * a.kv_sh;
   const bf16_t* vp = (const bf16_t*)a.v + b * a.kv_sb + kvh * a.kv_sh;
 
+  // Tile sequence: dense = t_lo .. t_hi-1; sparse = the two 64-key halves of each listed
+  // 128-key block, restricted to [t_lo, t_hi) (a contiguous run, the list is ascending).
+  const int32_t* lst = nullptr;
+  int n0 = 0, n1 = 0;
+  if (SPARSE) {
+    lst = a.block_list + ((int64_t)(b * a.Hq + h) * a.n_qb + qt) * a.list_stride;
+    const int cnt = lst[0];
+    n1 = 2 * cnt;
+    while (n0 < n1 && 2 * lst[1 + (n0 >> 1)] + (n0 & 1) < t_lo) ++n0;
+    int e = n0;
+    while (e < n1 && 2 * lst[1 + (e >> 1)] + (e & 1) < t_hi) ++e;
+    n1 = e;
+  } else {
+    n1 = max(0, t_hi - t_lo);
+  }
+  auto tile_of = [&](int n) -> int { return SPARSE ? 2 * lst[1 + (n >> 1)] + (n & 1) : t_lo + n; };
+
+  // HBM -> LDS for one tile: wave w fills 1 KB blocks 4w..4w+3 (rows 16w..16w+15) of K and V.
+  auto issue_tile = [&](int t, int buf) {
+    const int jb = t * KT;
+    bf16_t* kdst = lds + buf * BUF_ELEMS;
+    bf16_t* vdst = kdst + TILE_ELEMS;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int blk = wave * 4 + i;
+      const int r = blk * 4 + (lane >> 4);
+      const int s = lane & 15;
+      const int64_t rg = min(jb + r, kv_hi - 1);
+      __builtin_amdgcn_global_load_lds((const void*)(kp + rg * a.kv_st + ((s ^ (r & 15)) << 3)),
+                                       (lds_void_ptr)(kdst + blk * 512), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vp + rg * a.kv_st + ((s ^ ((r & 3) << 2)) << 3)),
+                                       (lds_void_ptr)(vdst + blk * 512), 16, 0, 0);
+    }
+  };
+
+  if (n0 < n1) issue_tile(tile_of(n0), 0);
+
   bf16x8 qf[8];
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
@@ -118,61 +170,22 @@ __global__ void __launch_bounds__(NTHR) prefill_bf16_d128(AttnArgs a) {
     m_run = a.sink[h] * kLog2e;
     l_run = hh == 0 ? 1.f : 0.f;
   }
+  const float c = a.scale_log2;
 
-  // Tile sequence: dense = t_lo .. t_hi-1; sparse = the two 64-key halves of each listed
-  // 128-key block, restricted to [t_lo, t_hi) (a contiguous run, the list is ascending).
-  const int32_t* lst = nullptr;
-  int n0 = 0, n1 = 0;
-  if (SPARSE) {
-    lst = a.block_list + ((int64_t)(b * a.Hq + h) * a.n_qb + qt) * a.list_stride;
-    const int cnt = lst[0];
-    n1 = 2 * cnt;
-    while (n0 < n1 && 2 * lst[1 + (n0 >> 1)] + (n0 & 1) < t_lo) ++n0;
-    int e = n0;
-    while (e < n1 && 2 * lst[1 + (e >> 1)] + (e & 1) < t_hi) ++e;
-    n1 = e;
-  } else {
-    n0 = 0;
-    n1 = max(0, t_hi - t_lo);
-  }
-  auto tile_of = [&](int n) -> int { return SPARSE ? 2 * lst[1 + (n >> 1)] + (n & 1) : t_lo + n; };
+  // V^T operand addressing (ds_read_b64_tr_b16): lane j of each 16-lane group points at
+  // row (4*hh + j/4) and columns t0 + 4*(j%4) .. +3 of a 4-key x 16-column block.
+  const int trj = lane & 15;
+  const int tr_row = 4 * hh + (trj >> 2);
+  const int tr_col = ((lane >> 4) & 1) * 16 + 4 * (trj & 3);
 
-  u32x4 kreg[4], vreg[4];
-  auto load_tile = [&](int t) {
-    const int jb = t * KT;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ci = tid + NTHR * i;
-      const int kk = ci >> 4, kc = ci & 15;  // K: 4 keys x 16 chunks per wave (coalesced)
-      const int vk = ci & 63, vc = ci >> 6;  // V: 64 keys x 1 chunk per wave
-      u32x4 z = {0u, 0u, 0u, 0u};
-      kreg[i] = (jb + kk < kv_hi) ? *(const u32x4*)(kp + (int64_t)(jb + kk) * a.kv_st + kc * 8) : z;
-      vreg[i] = (jb + vk < kv_hi) ? *(const u32x4*)(vp + (int64_t)(jb + vk) * a.kv_st + vc * 8) : z;
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ci = tid + NTHR * i;
-      const int kk = ci >> 4, kc = ci & 15;
-      *(u32x4*)(k_lds + kk * D + ((kc ^ (kk & 15)) << 3)) = kreg[i];
-      const int vk = ci & 63, vc = ci >> 6;
-      const int col = vt_col(vk);
-      const u32x4 w = vreg[i];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vt_lds[(vc * 8 + 2 * e) * VST + col] = __builtin_bit_cast(bf16_t, (uint16_t)(w[e] & 0xffffu));
-        vt_lds[(vc * 8 + 2 * e + 1) * VST + col] = __builtin_bit_cast(bf16_t, (uint16_t)(w[e] >> 16));
-      }
-    }
-  };
-
-  if (n0 < n1) load_tile(tile_of(n0));
+  wait_vmem();
+  __syncthreads();
   for (int n = n0; n < n1; ++n) {
+    const int buf = (n - n0) & 1;
     const int t = tile_of(n);
-    store_tile();
-    __syncthreads();
-    if (n + 1 < n1) load_tile(tile_of(n + 1));
+    if (n + 1 < n1) issue_tile(tile_of(n + 1), buf ^ 1);
+    const bf16_t* kt = lds + buf * BUF_ELEMS;
+    const bf16_t* vt = kt + TILE_ELEMS;
 
     const int j0 = t * KT;
     const bool skip = !wave_active || j0 > wpos_hi || (a.window > 0 && j0 + KT - 1 <= wpos_lo - a.window);
@@ -183,57 +196,64 @@ __global__ void __launch_bounds__(NTHR) prefill_bf16_d128(AttnArgs a) {
       for (int v = 0; v < 16; ++v) { s0[v] = 0.f; s1[v] = 0.f; }
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        const int sw = ((2 * ks + hh) ^ (l32 & 15)) << 3;
-        const bf16x8 ka = *(const bf16x8*)(k_lds + l32 * D + sw);
-        const bf16x8 kb = *(const bf16x8*)(k_lds + (32 + l32) * D + sw);
+        const bf16x8 ka = *(const bf16x8*)(kt + k_off(l32, 2 * ks + hh));
+        const bf16x8 kb = *(const bf16x8*)(kt + k_off(32 + l32, 2 * ks + hh));
         s0 = mfma32x32x16(ka, qf[ks], s0);
         s1 = mfma32x32x16(kb, qf[ks], s1);
       }
-      float x[32];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        x[v] = s0[v] * a.scale_log2;
-        x[16 + v] = s1[v] * a.scale_log2;
-      }
       if (need_mask) {
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          const int j = j0 + (i >> 4) * 32 + 8 * ((i & 15) >> 2) + 4 * hh + (i & 3);
-          const bool ok = j <= my_pos && (a.window <= 0 || j > my_pos - a.window);
-          x[i] = ok ? x[i] : SOC_NEG_INF;
+        for (int i = 0; i < 16; ++i) {
+          const int j = j0 + 8 * (i >> 2) + 4 * hh + (i & 3);
+          const bool ok0 = j <= my_pos && (a.window <= 0 || j > my_pos - a.window);
+          const bool ok1 = j + 32 <= my_pos && (a.window <= 0 || j + 32 > my_pos - a.window);
+          s0[i] = ok0 ? s0[i] : SOC_NEG_INF;
+          s1[i] = ok1 ? s1[i] : SOC_NEG_INF;
         }
       }
-      float mx = x[0];
+      float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
-      for (int i = 1; i < 32; ++i) mx = fmaxf(mx, x[i]);
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
       mx = fmaxf(mx, swap_halves(mx));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = (m_new == SOC_NEG_INF) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      float lsum = 0.f;
+      const float m_cand = mx * c;
+      const bool upd = m_cand > m_run + RESCALE_SLACK;
+      if (__builtin_amdgcn_ballot_w64(upd) != 0) {
+        // lanes that do not raise their max keep alpha = 1 (their m_run may still be -inf)
+        const float m_new = upd ? m_cand : m_run;
+        const float alpha = upd ? fast_exp2(m_run - m_new) : 1.f;
+        l_run *= alpha;
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        x[i] = fast_exp2(x[i] - m_use);
-        lsum += x[i];
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) oacc[tb][v] *= alpha;
+        m_run = m_new;
       }
-      l_run = l_run * alpha + lsum;
-      m_run = m_new;
+      const float nm = (m_run == SOC_NEG_INF) ? 0.f : -m_run;
+      float lsum = 0.f;
+      bf16x8 pb[4];
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) oacc[tb][v] *= alpha;
+      for (int i = 0; i < 16; ++i) {
+        const float p0 = fast_exp2(fmaf(s0[i], c, nm));
+        const float p1 = fast_exp2(fmaf(s1[i], c, nm));
+        lsum += p0 + p1;
+        pb[i >> 3][i & 7] = (bf16_t)p0;
+        pb[2 + (i >> 3)][i & 7] = (bf16_t)p1;
+      }
+      l_run += lsum;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        bf16x8 pb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pb[e] = (bf16_t)x[kk * 8 + e];
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
-          const bf16x8 va = *(const bf16x8*)(vt_lds + (tb * 32 + l32) * VST + 16 * kk + 8 * hh);
-          oacc[tb] = mfma32x32x16(va, pb, oacc[tb]);
+          const int row = 16 * kk + tr_row;
+          const int col = tb * 32 + tr_col;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vt + v_off(row, col >> 3) + (col & 7)));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vt + v_off(row + 8, col >> 3) + (col & 7)));
+          const s16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          oacc[tb] = mfma32x32x16(__builtin_bit_cast(bf16x8, va), pb[kk], oacc[tb]);
         }
       }
     }
+    wait_vmem();
     __syncthreads();
   }
 
