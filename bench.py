@@ -206,7 +206,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="all", help="all | causal_prefill | window_sink | decode | block_sparse")
+    ap.add_argument("--only", default="all",
+                    help="all | causal_prefill | window_sink | decode | block_sparse | copy (HBM counter calibration)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=None, help="JSON file with measured HBM bytes per launch of the prefill kernel")
     args = ap.parse_args()
@@ -221,6 +222,17 @@ def main():
 
     def log(msg):
         print(msg, file=sys.stderr, flush=True)
+
+    if args.only == "copy":
+        # A plain device-to-device copy of known size: HBM byte counters read on it give the
+        # scale factor between counted and true bytes.
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        r = Timer(lambda: dst.copy_(src), args.steps, args.warmup).run()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms": r["launch_ms_mean"],
+                          "GBps_read_plus_write": 2 * n / (r["launch_ms_mean"] * 1e-3) / 1e9}), flush=True)
+        return
 
     also = {}
     head = None

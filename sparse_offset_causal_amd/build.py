@@ -20,6 +20,10 @@ SOURCES = ["abi.cpp", "prefill_bf16.hip", "decode_bf16.hip", "attn_f32.hip", "bl
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", INCLUDE, "-I", CSRC]
+# Kernel sources only: no kernel reads or produces NaN on purpose, so min/max need no NaN
+# quieting; infinities keep their IEEE meaning.  The host-side argument checks (abi.cpp,
+# which tests for NaN) are compiled without these.
+KERNEL_FLAGS = ["-fno-honor-nans", "-mno-amdgpu-ieee"]
 
 
 def hipcc() -> str:
@@ -31,7 +35,8 @@ def hipcc() -> str:
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    extra = KERNEL_FLAGS if src.endswith(".hip") else []
+    cmd = [hipcc(), *FLAGS, *extra, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

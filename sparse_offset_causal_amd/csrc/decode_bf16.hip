@@ -28,7 +28,10 @@ namespace {
 
 constexpr int D = 128;
 constexpr int KB = 32;                 // keys per block
-constexpr int NST = 4;                 // ring stages
+#ifndef SOC_DECODE_STAGES
+#define SOC_DECODE_STAGES 4
+#endif
+constexpr int NST = SOC_DECODE_STAGES;  // ring stages (NST * 16 KB of LDS per wave)
 constexpr int HALF = KB * D;           // K (or V) elements of one stage
 constexpr int STAGE = 2 * HALF;        // 16 KB
 constexpr float RESCALE_SLACK = 8.0f;
@@ -43,6 +46,7 @@ __device__ __forceinline__ int v_off(int row, int chunk) { return row * D + ((ch
 
 // Wait until at most `blocks_after` blocks (16 DMA instructions each) are still in flight.
 __device__ __forceinline__ void wait_blocks(int blocks_after) {
+  static_assert(NST >= 2 && NST <= 4, "vmcnt holds at most 63 outstanding loads: 3 blocks of 16");
   if (blocks_after >= 3)
     asm volatile("s_waitcnt vmcnt(48)" ::: "memory");
   else if (blocks_after == 2)
@@ -138,7 +142,7 @@ __global__ void __launch_bounds__(64) decode_split_bf16_d128(AttnArgs a) {
       sacc[v] = ok ? sacc[v] : SOC_NEG_INF;
       mx = fmaxf(mx, sacc[v]);
     }
-    mx = fmaxf(mx, swap_halves(mx));
+    mx = pair_max(mx);
     const float m_cand = mx * c;
     const bool upd = m_cand > m_run + RESCALE_SLACK;
     if (__builtin_amdgcn_ballot_w64(upd) != 0) {
@@ -173,7 +177,7 @@ __global__ void __launch_bounds__(64) decode_split_bf16_d128(AttnArgs a) {
     asm volatile("" ::: "memory");  // this stage's LDS reads stay ahead of its next refill
   }
 
-  const float L = l_run + swap_halves(l_run);
+  const float L = pair_sum(l_run);
   if (row_ok) {
     const int64_t rowid = ((int64_t)b * a.Hq + h) * a.tq + r;
     float* po = a.part + (rowid * a.nsplit + s) * D;

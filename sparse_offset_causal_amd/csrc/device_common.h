@@ -32,9 +32,18 @@ __device__ __forceinline__ u32x4 as_u32x4(bf16x8 x) { return __builtin_bit_cast(
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
-// Swap of lanes l and l^32 (the two halves of a wave64).
-__device__ __forceinline__ float swap_halves(float x) {
-  return __shfl_xor(x, 32, 64);
+// Lanes l and l^32 (the two halves of a wave64) exchange a value with gfx950's
+// v_permlane32_swap; with both operands = x the pair comes back as {x[l & 31], x[l | 32]},
+// so symmetric combinations of the pair give the same result in both lanes.
+__device__ __forceinline__ float pair_max(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
+                                                  false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)p[0]), __builtin_bit_cast(float, (unsigned)p[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
+                                                  false, false);
+  return __builtin_bit_cast(float, (unsigned)p[0]) + __builtin_bit_cast(float, (unsigned)p[1]);
 }
 
 // Order-preserving map of doubles to unsigned 64-bit keys (ascending).

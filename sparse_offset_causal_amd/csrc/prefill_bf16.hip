@@ -36,6 +36,8 @@
 // is a multiple of 8, each XCD is given whole KV groups (their K/V stay in that XCD's L2),
 // and within an XCD the query tiles with the most keys are dispatched first.
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -172,19 +174,31 @@ prefill_bf16_d128(AttnArgs a) {
   }
   const float c = a.scale_log2;
 
-  // V^T operand addressing (ds_read_b64_tr_b16): lane j of each 16-lane group points at
-  // row (4*hh + j/4) and columns t0 + 4*(j%4) .. +3 of a 4-key x 16-column block.
-  const int trj = lane & 15;
-  const int tr_row = 4 * hh + (trj >> 2);
-  const int tr_col = ((lane >> 4) & 1) * 16 + 4 * (trj & 3);
+  // Per-lane LDS element offsets, fixed for the whole kernel, so that every LDS read in the
+  // loop is one of these plus an immediate (second key block, kk, hi/lo, buffer).
+  //   K (A operand of S^T): key l32 (+32), chunk 2*ks + hh.
+  //   V (ds_read_b64_tr_b16): lane j of each 16-lane group points at key 4*hh + j/4 (+16kk, +8)
+  //   and columns tb*32 + 16*((lane>>4)&1) + 4*(j%4) .. +3; the row's swizzle term 4*(row&3)
+  //   depends only on the lane, so only the chunk part varies with tb.
+  int koff[8], voff[4];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) koff[ks] = k_off(l32, 2 * ks + hh);
+  {
+    const int trj = lane & 15;
+    const int tr_row = 4 * hh + (trj >> 2);
+    const int tr_col = ((lane >> 4) & 1) * 16 + 4 * (trj & 3);
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      const int col = tb * 32 + tr_col;
+      voff[tb] = v_off(tr_row, col >> 3) + (col & 7);
+    }
+  }
 
-  wait_vmem();
-  __syncthreads();
-  for (int n = n0; n < n1; ++n) {
-    const int buf = (n - n0) & 1;
+  auto tile_step = [&](int n, auto buf_tag) {
+    constexpr int BUF = decltype(buf_tag)::value;
     const int t = tile_of(n);
-    if (n + 1 < n1) issue_tile(tile_of(n + 1), buf ^ 1);
-    const bf16_t* kt = lds + buf * BUF_ELEMS;
+    if (n + 1 < n1) issue_tile(tile_of(n + 1), BUF ^ 1);
+    const bf16_t* kt = lds + BUF * BUF_ELEMS;
     const bf16_t* vt = kt + TILE_ELEMS;
 
     const int j0 = t * KT;
@@ -196,25 +210,24 @@ prefill_bf16_d128(AttnArgs a) {
       for (int v = 0; v < 16; ++v) { s0[v] = 0.f; s1[v] = 0.f; }
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 ka = *(const bf16x8*)(kt + k_off(l32, 2 * ks + hh));
-        const bf16x8 kb = *(const bf16x8*)(kt + k_off(32 + l32, 2 * ks + hh));
-        s0 = mfma32x32x16(ka, qf[ks], s0);
-        s1 = mfma32x32x16(kb, qf[ks], s1);
+        s0 = mfma32x32x16(*(const bf16x8*)(kt + koff[ks]), qf[ks], s0);
+        s1 = mfma32x32x16(*(const bf16x8*)(kt + 32 * D + koff[ks]), qf[ks], s1);
       }
       if (need_mask) {
+        // key offset e (from j0) of this lane's row is visible iff lo_lim < e <= hi_lim
+        const int hi_lim = my_pos - j0;
+        const int lo_lim = a.window > 0 ? my_pos - a.window - j0 : -(1 << 30);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int j = j0 + 8 * (i >> 2) + 4 * hh + (i & 3);
-          const bool ok0 = j <= my_pos && (a.window <= 0 || j > my_pos - a.window);
-          const bool ok1 = j + 32 <= my_pos && (a.window <= 0 || j + 32 > my_pos - a.window);
-          s0[i] = ok0 ? s0[i] : SOC_NEG_INF;
-          s1[i] = ok1 ? s1[i] : SOC_NEG_INF;
+          const int e = 8 * (i >> 2) + 4 * hh + (i & 3);
+          s0[i] = (e <= hi_lim) & (e > lo_lim) ? s0[i] : SOC_NEG_INF;
+          s1[i] = (e + 32 <= hi_lim) & (e + 32 > lo_lim) ? s1[i] : SOC_NEG_INF;
         }
       }
       float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
       for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
-      mx = fmaxf(mx, swap_halves(mx));
+      mx = pair_max(mx);
       const float m_cand = mx * c;
       const bool upd = m_cand > m_run + RESCALE_SLACK;
       if (__builtin_amdgcn_ballot_w64(upd) != 0) {
@@ -244,10 +257,8 @@ prefill_bf16_d128(AttnArgs a) {
       for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) {
-          const int row = 16 * kk + tr_row;
-          const int col = tb * 32 + tr_col;
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vt + v_off(row, col >> 3) + (col & 7)));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vt + v_off(row + 8, col >> 3) + (col & 7)));
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vt + 16 * kk * D + voff[tb]));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vt + (16 * kk + 8) * D + voff[tb]));
           const s16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           oacc[tb] = mfma32x32x16(__builtin_bit_cast(bf16x8, va), pb[kk], oacc[tb]);
         }
@@ -255,9 +266,16 @@ prefill_bf16_d128(AttnArgs a) {
     }
     wait_vmem();
     __syncthreads();
+  };
+
+  wait_vmem();
+  __syncthreads();
+  for (int n = n0; n < n1; n += 2) {
+    tile_step(n, std::integral_constant<int, 0>{});
+    if (n + 1 < n1) tile_step(n + 1, std::integral_constant<int, 1>{});
   }
 
-  const float lt = l_run + swap_halves(l_run);
+  const float lt = pair_sum(l_run);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (my_row < a.tq) {
     bf16_t* op = (bf16_t*)a.o + b * a.o_sb + h * a.o_sh + (int64_t)my_row * a.o_st;
