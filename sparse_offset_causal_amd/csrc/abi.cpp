@@ -178,6 +178,8 @@ int attn_prefill(const attn_shape_t* shape, const void* q, attn_strides_t q_stri
   }
   const int64_t nqt = (shape->tq + 127) / 128;
   if (nqt * shape->batch * shape->n_heads >= (int64_t)1 << 31) return fail(ATTN_E_INVAL, "problem too large for one grid");
+  if (shape->dtype == ATTN_BF16 && (int64_t)shape->tk * kv_strides.t * 2 > (int64_t)0xffffffff)
+    return fail(ATTN_E_UNSUPPORTED, "one (sequence, KV head) cache slice spans more than 4 GiB (tk * token stride)");
   if ((rc = check_offsets_debug(shape, cache_off, stream))) return rc;
 
   soc::AttnArgs a = make_args(shape, q, q_strides, k, v, kv_strides, o, o_strides, cache_off, window, sink, scale);
@@ -211,6 +213,8 @@ int attn_decode(const attn_shape_t* shape, const void* q, attn_strides_t q_strid
     return ATTN_OK;
   }
   if ((rc = check_tensors(shape, q, q_strides, k, v, kv_strides, o, o_strides))) return rc;
+  if (shape->dtype == ATTN_BF16 && (int64_t)shape->tk * kv_strides.t * 2 > (int64_t)0xffffffff)
+    return fail(ATTN_E_UNSUPPORTED, "one (sequence, KV head) cache slice spans more than 4 GiB (tk * token stride)");
   if (shape->dtype == ATTN_BF16 && (shape->n_heads / shape->n_kv) * shape->tq > 32)
     return fail(ATTN_E_UNSUPPORTED, "bf16 decode serves at most 32 query rows per KV head ((n_heads/n_kv)*tq <= 32)");
   const int split = split_tokens > 0 ? split_tokens : default_split(shape);

@@ -146,6 +146,7 @@ __global__ void __launch_bounds__(64) decode_split_bf16_d128(AttnArgs a) {
     const float m_cand = mx * c;
     const bool upd = m_cand > m_run + RESCALE_SLACK;
     if (__builtin_amdgcn_ballot_w64(upd) != 0) {
+      asm volatile("");  // keeps this a branch: the rescale is rare, never speculate it
       const float m_new = upd ? m_cand : m_run;
       const float alpha = upd ? fast_exp2(m_run - m_new) : 1.f;
       l_run *= alpha;

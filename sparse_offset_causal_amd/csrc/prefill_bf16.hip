@@ -29,8 +29,10 @@
 //   operand with ds_read_b128 (chunk' = chunk ^ (row & 15): 16 consecutive keys hit 16
 //   distinct bank groups).  V is read already transposed with ds_read_b64_tr_b16 (each
 //   16-lane group reads a 4-key x 16-column block; chunk' = chunk ^ 4*(row & 3) makes the
-//   two groups of a half-wave cover all 64 banks once).  Rows past the last visible key
-//   are clamped to a valid row: their scores are masked, their probabilities are exactly 0.
+//   two groups of a half-wave cover all 64 banks once).  The loads are buffer loads whose
+//   range ends at the last row any query of the workgroup may see: later rows read as zero
+//   and are masked.  All LDS and DMA addressing is per-lane offsets fixed at kernel start
+//   plus immediates or one scalar per tile.
 //
 // Grid order: workgroup i runs on XCD i % 8.  When the number of KV groups (batch x n_kv)
 // is a multiple of 8, each XCD is given whole KV groups (their K/V stay in that XCD's L2),
@@ -98,8 +100,12 @@ prefill_bf16_d128(AttnArgs a) {
   const int n_qt = (a.tq + QT - 1) / QT;
   int qt, h, b;
   map_block(blockIdx.x, a, n_qt, qt, h, b);
-  const int kvh = h / a.g;
-  const int off = a.cache_off ? a.cache_off[b] : a.tk - a.tq;
+  qt = __builtin_amdgcn_readfirstlane(qt);  // integer division leaves these in VGPRs
+  h = __builtin_amdgcn_readfirstlane(h);
+  b = __builtin_amdgcn_readfirstlane(b);
+  const int kvh = __builtin_amdgcn_readfirstlane(h / a.g);
+  // Per-workgroup scalars are made provably wave-uniform so tile-level branches stay scalar.
+  const int off = __builtin_amdgcn_readfirstlane(a.cache_off ? a.cache_off[b] : a.tk - a.tq);
   const int tkb = off + a.tq;
   const int row0 = qt * QT;
   const int rowl = min(row0 + QT, a.tq) - 1;
@@ -133,23 +139,34 @@ prefill_bf16_d128(AttnArgs a) {
   } else {
     n1 = max(0, t_hi - t_lo);
   }
-  auto tile_of = [&](int n) -> int { return SPARSE ? 2 * lst[1 + (n >> 1)] + (n & 1) : t_lo + n; };
+  auto tile_of = [&](int n) __attribute__((always_inline)) -> int {
+    return SPARSE ? __builtin_amdgcn_readfirstlane(2 * lst[1 + (n >> 1)] + (n & 1)) : t_lo + n;
+  };
 
   // HBM -> LDS for one tile: wave w fills 1 KB blocks 4w..4w+3 (rows 16w..16w+15) of K and V.
-  auto issue_tile = [&](int t, int buf) {
-    const int jb = t * KT;
+  // Buffer loads with a per-lane byte offset fixed for the kernel (row in tile, swizzled
+  // chunk) and the tile's first row in the scalar offset; rows at or beyond kv_hi fall
+  // outside the buffer's range and read as zero.
+  const uint32_t row_bytes = (uint32_t)a.kv_st * 2u;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kp, (short)0, (int)(kv_hi * row_bytes), 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vp, (short)0, (int)(kv_hi * row_bytes), 0x00020000);
+  uint32_t kdma[4], vdma[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = (wave * 4 + i) * 4 + (lane >> 4);
+    const int sl = lane & 15;
+    kdma[i] = r * row_bytes + (uint32_t)((sl ^ (r & 15)) << 4);
+    vdma[i] = r * row_bytes + (uint32_t)((sl ^ ((r & 3) << 2)) << 4);
+  }
+  auto issue_tile = [&](int t, int buf) __attribute__((always_inline)) {
+    const uint32_t tile_off = (uint32_t)(t * KT) * row_bytes;
     bf16_t* kdst = lds + buf * BUF_ELEMS;
     bf16_t* vdst = kdst + TILE_ELEMS;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int blk = wave * 4 + i;
-      const int r = blk * 4 + (lane >> 4);
-      const int s = lane & 15;
-      const int64_t rg = min(jb + r, kv_hi - 1);
-      __builtin_amdgcn_global_load_lds((const void*)(kp + rg * a.kv_st + ((s ^ (r & 15)) << 3)),
-                                       (lds_void_ptr)(kdst + blk * 512), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(vp + rg * a.kv_st + ((s ^ ((r & 3) << 2)) << 3)),
-                                       (lds_void_ptr)(vdst + blk * 512), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void_ptr)(kdst + blk * 512), 16, kdma[i], tile_off, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void_ptr)(vdst + blk * 512), 16, vdma[i], tile_off, 0, 0);
     }
   };
 
@@ -194,7 +211,70 @@ prefill_bf16_d128(AttnArgs a) {
     }
   }
 
-  auto tile_step = [&](int n, auto buf_tag) {
+  auto compute_tile = [&](const bf16_t* kt, const bf16_t* vt, int j0, bool need_mask) __attribute__((always_inline)) {
+    f32x16 s0, s1;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) { s0[v] = 0.f; s1[v] = 0.f; }
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      s0 = mfma32x32x16(*(const bf16x8*)(kt + koff[ks]), qf[ks], s0);
+      s1 = mfma32x32x16(*(const bf16x8*)(kt + 32 * D + koff[ks]), qf[ks], s1);
+    }
+    if (need_mask) {
+      asm volatile("");  // keeps this a branch: only tiles on a causal or window edge pay for it
+      // key offset e (from j0) of this lane's row is visible iff lo_lim < e <= hi_lim
+      const int hi_lim = my_pos - j0;
+      const int lo_lim = a.window > 0 ? my_pos - a.window - j0 : -(1 << 30);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int e = 8 * (i >> 2) + 4 * hh + (i & 3);
+        s0[i] = (e <= hi_lim) & (e > lo_lim) ? s0[i] : SOC_NEG_INF;
+        s1[i] = (e + 32 <= hi_lim) & (e + 32 > lo_lim) ? s1[i] : SOC_NEG_INF;
+      }
+    }
+    float mx = fmaxf(s0[0], s1[0]);
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
+    mx = pair_max(mx);
+    const float m_cand = mx * c;
+    const bool upd = m_cand > m_run + RESCALE_SLACK;
+    if (__builtin_amdgcn_ballot_w64(upd) != 0) {
+      asm volatile("");  // keeps this a branch: the rescale is rare, never speculate it
+      // lanes that do not raise their max keep alpha = 1 (their m_run may still be -inf)
+      const float m_new = upd ? m_cand : m_run;
+      const float alpha = upd ? fast_exp2(m_run - m_new) : 1.f;
+      l_run *= alpha;
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) oacc[tb][v] *= alpha;
+      m_run = m_new;
+    }
+    const float nm = (m_run == SOC_NEG_INF) ? 0.f : -m_run;
+    float lsum = 0.f;
+    bf16x8 pb[4];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float p0 = fast_exp2(fmaf(s0[i], c, nm));
+      const float p1 = fast_exp2(fmaf(s1[i], c, nm));
+      lsum += p0 + p1;
+      pb[i >> 3][i & 7] = (bf16_t)p0;
+      pb[2 + (i >> 3)][i & 7] = (bf16_t)p1;
+    }
+    l_run += lsum;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vt + 16 * kk * D + voff[tb]));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vt + (16 * kk + 8) * D + voff[tb]));
+        const s16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        oacc[tb] = mfma32x32x16(__builtin_bit_cast(bf16x8, va), pb[kk], oacc[tb]);
+      }
+    }
+  };
+
+  auto tile_step = [&](int n, auto buf_tag) __attribute__((always_inline)) {
     constexpr int BUF = decltype(buf_tag)::value;
     const int t = tile_of(n);
     if (n + 1 < n1) issue_tile(tile_of(n + 1), BUF ^ 1);
@@ -204,65 +284,9 @@ prefill_bf16_d128(AttnArgs a) {
     const int j0 = t * KT;
     const bool skip = !wave_active || j0 > wpos_hi || (a.window > 0 && j0 + KT - 1 <= wpos_lo - a.window);
     if (!skip) {
+      // Only tiles that cross a row's causal limit or window edge apply the index mask.
       const bool need_mask = (j0 + KT - 1 > wpos_lo) || (a.window > 0 && j0 <= wpos_hi - a.window);
-      f32x16 s0, s1;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) { s0[v] = 0.f; s1[v] = 0.f; }
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        s0 = mfma32x32x16(*(const bf16x8*)(kt + koff[ks]), qf[ks], s0);
-        s1 = mfma32x32x16(*(const bf16x8*)(kt + 32 * D + koff[ks]), qf[ks], s1);
-      }
-      if (need_mask) {
-        // key offset e (from j0) of this lane's row is visible iff lo_lim < e <= hi_lim
-        const int hi_lim = my_pos - j0;
-        const int lo_lim = a.window > 0 ? my_pos - a.window - j0 : -(1 << 30);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int e = 8 * (i >> 2) + 4 * hh + (i & 3);
-          s0[i] = (e <= hi_lim) & (e > lo_lim) ? s0[i] : SOC_NEG_INF;
-          s1[i] = (e + 32 <= hi_lim) & (e + 32 > lo_lim) ? s1[i] : SOC_NEG_INF;
-        }
-      }
-      float mx = fmaxf(s0[0], s1[0]);
-#pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
-      mx = pair_max(mx);
-      const float m_cand = mx * c;
-      const bool upd = m_cand > m_run + RESCALE_SLACK;
-      if (__builtin_amdgcn_ballot_w64(upd) != 0) {
-        // lanes that do not raise their max keep alpha = 1 (their m_run may still be -inf)
-        const float m_new = upd ? m_cand : m_run;
-        const float alpha = upd ? fast_exp2(m_run - m_new) : 1.f;
-        l_run *= alpha;
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) oacc[tb][v] *= alpha;
-        m_run = m_new;
-      }
-      const float nm = (m_run == SOC_NEG_INF) ? 0.f : -m_run;
-      float lsum = 0.f;
-      bf16x8 pb[4];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p0 = fast_exp2(fmaf(s0[i], c, nm));
-        const float p1 = fast_exp2(fmaf(s1[i], c, nm));
-        lsum += p0 + p1;
-        pb[i >> 3][i & 7] = (bf16_t)p0;
-        pb[2 + (i >> 3)][i & 7] = (bf16_t)p1;
-      }
-      l_run += lsum;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vt + 16 * kk * D + voff[tb]));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vt + (16 * kk + 8) * D + voff[tb]));
-          const s16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          oacc[tb] = mfma32x32x16(__builtin_bit_cast(bf16x8, va), pb[kk], oacc[tb]);
-        }
-      }
+      compute_tile(kt, vt, j0, need_mask);
     }
     wait_vmem();
     __syncthreads();
