@@ -123,7 +123,7 @@ soc::AttnArgs make_args(const attn_shape_t* s, const void* q, attn_strides_t qs,
 // Keys per decode split: long splits amortise each wave's pipeline start-up; shorter ones
 // keep at least ~1024 workgroups (two per CU slot, four rounds) when the batch is small.
 int default_split(const attn_shape_t* s) {
-  int split = 4096;
+  int split = 2048;
   while (split > 256 && (int64_t)s->batch * s->n_kv * ((s->tk + split - 1) / split) < 1024) split /= 2;
   return split;
 }

@@ -6,19 +6,23 @@
 // serves all g = n_heads / n_kv query heads x tq rows of that group (<= 32 rows) from a
 // single read of the split's K and V: K/V bytes cross HBM exactly once per call.
 //
-// A workgroup is one wave.  It streams its split in 32-key blocks through a private ring of
-// NST LDS stages (16 KB each: K then V, row-major with the same 16-byte-chunk XOR swizzles
-// as the prefill kernel) filled by HBM -> LDS DMA (global_load_lds_dwordx4), keeping
-// NST-1 blocks in flight while it consumes one; being alone in its workgroup, it only waits
-// on its own vector-memory counter, never on a barrier.  Per block it computes
-// S^T = K Q^T (query rows are the MFMA's N columns, padded to 32) and O^T += V^T P^T with
-// v_mfma_f32_32x32x16_bf16, V read transposed by ds_read_b64_tr_b16, with an online softmax
-// in the log2 domain (running max raised only when it grows by more than 2^8).  The split's
-// unnormalised partial (max, sum, O) is written in fp32.  The sink is not applied here;
-// the merge adds it exactly once per row.
+// A workgroup is one wave.  It streams its split in 32-key blocks, keeping NST-1 blocks in
+// flight while it consumes one: K goes HBM -> registers directly, already in the MFMA
+// A-operand layout (lane = key, 16-byte chunks of its row), and V goes HBM -> LDS by DMA
+// (buffer_load ... lds, row-major with a 16-byte-chunk XOR swizzle) for the transposed
+// read.  With only V in LDS (8 KB per stage) several such waves fit on a CU, which is what
+// keeps enough bytes in flight to stream the cache at HBM rate.  Being alone in its
+// workgroup, a wave only waits on its own vector-memory counter, never on a barrier.  Per
+// block it computes S^T = K Q^T (query rows are the MFMA's N columns, padded to 32) and
+// O^T += V^T P^T with v_mfma_f32_32x32x16_bf16, V read transposed by ds_read_b64_tr_b16,
+// with an online softmax in the log2 domain (running max raised only when it grows by more
+// than 2^8).  The split's unnormalised partial (max, sum, O) is written in fp32.  The sink is
+// not applied here; the merge adds it exactly once per row.
 //
 // Merge: per (b, h, r) row, M = max(max_s m_s, sink), L = sum_s l_s 2^(m_s - M) + 2^(sink - M),
 // o = sum_s o_s 2^(m_s - M) / L (all in the log2 domain), rounded once to the output type.
+
+#include <type_traits>
 
 #include "device_common.h"
 #include "internal.h"
@@ -27,13 +31,9 @@ namespace soc {
 namespace {
 
 constexpr int D = 128;
-constexpr int KB = 32;                 // keys per block
-#ifndef SOC_DECODE_STAGES
-#define SOC_DECODE_STAGES 4
-#endif
-constexpr int NST = SOC_DECODE_STAGES;  // ring stages (NST * 16 KB of LDS per wave)
-constexpr int HALF = KB * D;           // K (or V) elements of one stage
-constexpr int STAGE = 2 * HALF;        // 16 KB
+constexpr int KB = 32;                  // keys per block
+constexpr int NST = 3;                  // blocks resident per wave: one consumed, NST-1 in flight
+constexpr int VSTAGE = KB * D;          // V elements of one LDS stage (8 KB)
 constexpr float RESCALE_SLACK = 8.0f;
 
 typedef short s16x4 __attribute__((__vector_size__(8)));
@@ -41,15 +41,12 @@ typedef short s16x8 __attribute__((__vector_size__(16)));
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
 
-__device__ __forceinline__ int k_off(int row, int chunk) { return row * D + ((chunk ^ (row & 15)) << 3); }
 __device__ __forceinline__ int v_off(int row, int chunk) { return row * D + ((chunk ^ ((row & 3) << 2)) << 3); }
 
-// Wait until at most `blocks_after` blocks (16 DMA instructions each) are still in flight.
+// Wait until at most `blocks_after` blocks (16 loads each: 8 of K, 8 of V) are still in flight.
 __device__ __forceinline__ void wait_blocks(int blocks_after) {
-  static_assert(NST >= 2 && NST <= 4, "vmcnt holds at most 63 outstanding loads: 3 blocks of 16");
-  if (blocks_after >= 3)
-    asm volatile("s_waitcnt vmcnt(48)" ::: "memory");
-  else if (blocks_after == 2)
+  static_assert(NST - 1 <= 3, "vmcnt holds at most 63 outstanding loads: 3 blocks of 16");
+  if (blocks_after >= 2)
     asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
   else if (blocks_after == 1)
     asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
@@ -57,15 +54,17 @@ __device__ __forceinline__ void wait_blocks(int blocks_after) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-__global__ void __launch_bounds__(64) decode_split_bf16_d128(AttnArgs a) {
-  __shared__ __attribute__((aligned(1024))) bf16_t lds[NST * STAGE];
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
+decode_split_bf16_d128(AttnArgs a) {
+  __shared__ __attribute__((aligned(1024))) bf16_t vlds[NST * VSTAGE];
 
   const int lane = threadIdx.x;
   const int l32 = lane & 31, hh = lane >> 5;
-  const int s = blockIdx.x % a.nsplit;
+  const int s = __builtin_amdgcn_readfirstlane(blockIdx.x % a.nsplit);
   const int rem = blockIdx.x / a.nsplit;
-  const int kvh = rem % a.Hkv, b = rem / a.Hkv;
-  const int off = a.cache_off ? a.cache_off[b] : a.tk - a.tq;
+  const int kvh = __builtin_amdgcn_readfirstlane(rem % a.Hkv);
+  const int b = __builtin_amdgcn_readfirstlane(rem / a.Hkv);
+  const int off = __builtin_amdgcn_readfirstlane(a.cache_off ? a.cache_off[b] : a.tk - a.tq);
   const int tkb = off + a.tq;
   const int nsb = (tkb + a.split - 1) / a.split;
   if (s >= nsb) return;  // the merge reads only splits below nsb
@@ -74,23 +73,29 @@ __global__ void __launch_bounds__(64) decode_split_bf16_d128(AttnArgs a) {
   const int kbeg = max(ks0, kv_lo), kend = ks1;
   const int nblk = kbeg < kend ? (kend - kbeg + KB - 1) / KB : 0;
 
+  // K and V through buffer resources whose range ends at the split's last key: later rows
+  // read as zero (and are masked).  K goes straight to registers in the MFMA A-operand
+  // layout (lane: key l32, chunks 2ks+hh), V goes HBM -> LDS by DMA for the transposed read.
+  const uint32_t row_bytes = (uint32_t)a.kv_st * 2u;
   const bf16_t* kp = (const bf16_t*)a.k + b * a.kv_sb + kvh * a.kv_sh;
   const bf16_t* vp = (const bf16_t*)a.v + b * a.kv_sb + kvh * a.kv_sh;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kp, (short)0, (int)(kend * row_bytes), 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vp, (short)0, (int)(kend * row_bytes), 0x00020000);
+  const uint32_t k_lane = l32 * row_bytes + hh * 16;
+  const int vr = lane >> 4;  // row within each 4-row DMA block
+  const uint32_t v_lane = vr * row_bytes + (uint32_t)(((lane & 15) ^ ((vr & 3) << 2)) << 4);
 
-  auto issue = [&](int n) {
-    const int jb = kbeg + n * KB;
-    bf16_t* kdst = lds + (n % NST) * STAGE;
-    bf16_t* vdst = kdst + HALF;
-    const int sl = lane & 15;
+  bf16x8 kreg[NST][8];
+  auto issue = [&](int n, auto stage_tag) __attribute__((always_inline)) {
+    constexpr int ST = decltype(stage_tag)::value;
+    const uint32_t blk_off = (uint32_t)(kbeg + n * KB) * row_bytes;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = 4 * i + (lane >> 4);
-      const int64_t rg = min(jb + r, kend - 1);
-      __builtin_amdgcn_global_load_lds((const void*)(kp + rg * a.kv_st + ((sl ^ (r & 15)) << 3)),
-                                       (lds_void_ptr)(kdst + i * 512), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(vp + rg * a.kv_st + ((sl ^ ((r & 3) << 2)) << 3)),
-                                       (lds_void_ptr)(vdst + i * 512), 16, 0, 0);
-    }
+    for (int ks = 0; ks < 8; ++ks)
+      kreg[ST][ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(krs, k_lane + ks * 32, blk_off, 0));
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void_ptr)(vlds + ST * VSTAGE + i * 512), 16, v_lane,
+                                               blk_off + 4 * i * row_bytes, 0, 0);
   };
 
   // query row of this lane: rho = head-in-group * tq + r
@@ -106,9 +111,10 @@ __global__ void __launch_bounds__(64) decode_split_bf16_d128(AttnArgs a) {
     u32x4 z = {0u, 0u, 0u, 0u};
     qf[ks] = row_ok ? *(const bf16x8*)(qp + 16 * ks + 8 * hh) : as_bf16x8(z);
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // only block loads are counted below
 
-  for (int n = 0; n < min(NST - 1, nblk); ++n) issue(n);
+  if (nblk > 0) issue(0, std::integral_constant<int, 0>{});
+  if (nblk > 1) issue(1, std::integral_constant<int, 1>{});
 
   f32x16 oacc[4];
 #pragma unroll
@@ -117,28 +123,35 @@ __global__ void __launch_bounds__(64) decode_split_bf16_d128(AttnArgs a) {
     for (int v = 0; v < 16; ++v) oacc[tb][v] = 0.f;
   float m_run = SOC_NEG_INF, l_run = 0.f;
   const float c = a.scale_log2;
-  const int trj = lane & 15;
-  const int tr_row = 4 * hh + (trj >> 2);
-  const int tr_col = ((lane >> 4) & 1) * 16 + 4 * (trj & 3);
+  int voff[4];
+  {
+    const int trj = lane & 15;
+    const int tr_row = 4 * hh + (trj >> 2);
+    const int tr_col = ((lane >> 4) & 1) * 16 + 4 * (trj & 3);
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      const int col = tb * 32 + tr_col;
+      voff[tb] = v_off(tr_row, col >> 3) + (col & 7);
+    }
+  }
 
-  for (int n = 0; n < nblk; ++n) {
-    if (n + NST - 1 < nblk) issue(n + NST - 1);
+  auto step = [&](int n, auto stage_tag) __attribute__((always_inline)) {
+    constexpr int ST = decltype(stage_tag)::value;
+    if (n + NST - 1 < nblk) issue(n + NST - 1, std::integral_constant<int, (ST + NST - 1) % NST>{});
     wait_blocks(min(NST - 1, nblk - 1 - n));
-    const bf16_t* kt = lds + (n % NST) * STAGE;
-    const bf16_t* vt = kt + HALF;
+    const bf16_t* vt = vlds + ST * VSTAGE;
     const int js = kbeg + n * KB;
 
     f32x16 sacc;
 #pragma unroll
     for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-      sacc = mfma32x32x16(*(const bf16x8*)(kt + k_off(l32, 2 * ks + hh)), qf[ks], sacc);
+    for (int ks = 0; ks < 8; ++ks) sacc = mfma32x32x16(kreg[ST][ks], qf[ks], sacc);
     float mx = SOC_NEG_INF;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int j = js + 8 * (v >> 2) + 4 * hh + (v & 3);
-      const bool ok = j < kend && j <= pos && (a.window <= 0 || j > pos - a.window);
+      const bool ok = (j < kend) & (j <= pos) & ((a.window <= 0) | (j > pos - a.window));
       sacc[v] = ok ? sacc[v] : SOC_NEG_INF;
       mx = fmaxf(mx, sacc[v]);
     }
@@ -168,14 +181,18 @@ __global__ void __launch_bounds__(64) decode_split_bf16_d128(AttnArgs a) {
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
-        const int row = 16 * kk + tr_row;
-        const int col = tb * 32 + tr_col;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vt + v_off(row, col >> 3) + (col & 7)));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vt + v_off(row + 8, col >> 3) + (col & 7)));
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vt + 16 * kk * D + voff[tb]));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vt + (16 * kk + 8) * D + voff[tb]));
         const s16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         oacc[tb] = mfma32x32x16(__builtin_bit_cast(bf16x8, va), pb[kk], oacc[tb]);
       }
-    asm volatile("" ::: "memory");  // this stage's LDS reads stay ahead of its next refill
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this stage's LDS reads finish before its refill
+  };
+
+  for (int n = 0; n < nblk; n += NST) {
+    step(n, std::integral_constant<int, 0>{});
+    if (n + 1 < nblk) step(n + 1, std::integral_constant<int, 1>{});
+    if (n + 2 < nblk) step(n + 2, std::integral_constant<int, 2>{});
   }
 
   const float L = pair_sum(l_run);
