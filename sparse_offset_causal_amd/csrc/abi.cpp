@@ -132,7 +132,7 @@ size_t round_up(size_t x, size_t m) { return (x + m - 1) / m * m; }
 
 struct SelectLayout {
   int nqb, nkb;
-  size_t qmean, cT, rad2, score, total;  // byte offsets and total
+  size_t qmean, cT, rad2, score, norm2, nmax, hpart, tflag, hist, ccount, pick, cand, total;  // byte offsets, total
 };
 
 SelectLayout select_layout(const attn_shape_t* s, int bs) {
@@ -148,7 +148,26 @@ SelectLayout select_layout(const attn_shape_t* s, int bs) {
   L.rad2 = off;
   off = round_up(off + d8 * s->batch * s->n_kv * L.nkb, 256);
   L.score = off;
-  off = round_up(off + d8 * s->batch * s->n_heads * L.nqb * L.nkb, 256);
+  const size_t bh = (size_t)s->batch * s->n_heads;
+  off = round_up(off + d8 * bh * L.nqb * L.nkb, 256);
+  L.norm2 = off;
+  off = round_up(off + d8 * (bh * L.nqb + (size_t)s->batch * s->n_kv * L.nkb), 256);
+  L.nmax = off;
+  off = round_up(off + d8 * (bh + (size_t)s->batch * s->n_kv), 256);
+  const size_t tiles = (size_t)((L.nqb + soc::kScoreTile - 1) / soc::kScoreTile) *
+                       ((L.nkb + soc::kScoreTile - 1) / soc::kScoreTile);
+  L.hpart = off;
+  off = round_up(off + sizeof(uint16_t) * bh * tiles * soc::kSelBuckets, 256);
+  L.tflag = off;
+  off = round_up(off + sizeof(uint32_t) * bh * tiles, 256);
+  L.hist = off;
+  off = round_up(off + sizeof(uint32_t) * bh * soc::kSelBuckets, 256);
+  L.ccount = off;
+  off = round_up(off + sizeof(uint32_t) * bh, 256);
+  L.pick = off;
+  off = round_up(off + sizeof(int64_t) * bh * 4, 256);
+  L.cand = off;
+  off = round_up(off + d8 * bh * L.nqb * L.nkb, 256);
   L.total = off;
   return L;
 }
@@ -276,6 +295,8 @@ int attn_block_select(const attn_shape_t* shape, const void* q, attn_strides_t q
   if ((int64_t)shape->batch * shape->n_heads * L.nqb >= (int64_t)1 << 31 ||
       (int64_t)shape->batch * shape->n_kv * L.nkb >= (int64_t)1 << 31)
     return fail(ATTN_E_INVAL, "problem too large for one grid");
+  if ((int64_t)L.nqb * L.nkb >= (int64_t)1 << 31)
+    return fail(ATTN_E_INVAL, "too many (query block, key block) pairs per head");
   if ((rc = check_offsets_debug(shape, cache_off, stream))) return rc;
 
   soc::SelectArgs a{};
@@ -306,6 +327,14 @@ int attn_block_select(const attn_shape_t* shape, const void* q, attn_strides_t q
   a.cT = reinterpret_cast<double*>(ws + L.cT);
   a.rad2 = reinterpret_cast<double*>(ws + L.rad2);
   a.score = reinterpret_cast<double*>(ws + L.score);
+  a.norm2 = reinterpret_cast<double*>(ws + L.norm2);
+  a.nmax = reinterpret_cast<double*>(ws + L.nmax);
+  a.hpart = reinterpret_cast<uint32_t*>(ws + L.hpart);
+  a.tflag = reinterpret_cast<uint32_t*>(ws + L.tflag);
+  a.hist = reinterpret_cast<uint32_t*>(ws + L.hist);
+  a.ccount = reinterpret_cast<uint32_t*>(ws + L.ccount);
+  a.pick = reinterpret_cast<int64_t*>(ws + L.pick);
+  a.cand = reinterpret_cast<double*>(ws + L.cand);
   const hipError_t e = soc::launch_block_select(a, shape->dtype == ATTN_BF16, stream);
   return finish(e, stream, "attn_block_select launch");
 }

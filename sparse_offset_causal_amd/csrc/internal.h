@@ -37,6 +37,11 @@ __host__ __device__ inline size_t decode_rows(const AttnArgs& a) { return (size_
 __host__ __device__ inline size_t decode_o_floats(const AttnArgs& a) { return decode_rows(a) * a.nsplit * a.d; }
 __host__ __device__ inline size_t decode_ml_floats(const AttnArgs& a) { return decode_rows(a) * a.nsplit * 2; }
 
+// Buckets of the per-head score histogram that narrows the order statistic, and the side of
+// the square tile of (query block, key block) scores one workgroup computes.
+constexpr int kSelBuckets = 4096;
+constexpr int kScoreTile = 64;
+
 struct SelectArgs {
   const void* q;
   const void* k;
@@ -54,6 +59,14 @@ struct SelectArgs {
   double* cT;          // workspace [B, Hkv, d, nkb]
   double* rad2;        // workspace [B, Hkv, nkb]
   double* score;       // workspace [B, Hq, nqb, nkb]
+  double* norm2;       // workspace [B, Hq, nqb] |qmean|^2 then [B, Hkv, nkb] |c|^2
+  double* nmax;        // workspace [B*Hq] max |qmean|^2 per head, then [B*Hkv] max |c|^2
+  uint32_t* hpart;     // workspace [B, Hq, score tiles, kSelBuckets / 2]  per-tile histograms (u16 pairs)
+  uint32_t* tflag;     // workspace [B, Hq, score tiles]  1 if the tile holds an admissible pair
+  uint32_t* hist;      // workspace [B, Hq, kSelBuckets]  value histogram of the admissible s1
+  uint32_t* ccount;    // workspace [B, Hq]  candidates gathered
+  int64_t* pick;       // workspace [B, Hq, 4]  (N, n, bucket, rank within bucket)
+  double* cand;        // workspace [B, Hq, nqb * nkb]  candidates of the order statistic
 };
 
 hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t s);
