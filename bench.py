@@ -200,6 +200,28 @@ def cpu_baseline(w, budget_s=15.0):
             "sample": f"{heads_done} of 32 query heads, all {T} rows each (float64 numpy/BLAS), {dt:.1f} s"}
 
 
+# ------------------------------------------------------------------ measured traffic
+def load_traffic(path):
+    """HBM bytes per launch (counter-measured, copy-calibrated) per workload, kept only for
+    kernels whose source is unchanged since the counters were taken (sha256 of the file)."""
+    import hashlib
+
+    if not path or not os.path.exists(path):
+        return {}
+    with open(path) as f:
+        data = json.load(f)
+    out = {}
+    for name, e in data.get("kernels", {}).items():
+        src = os.path.join(ROOT, "sparse_offset_causal_amd", "csrc", e["source"])
+        if not os.path.exists(src):
+            continue
+        with open(src, "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != e["source_sha256"]:
+                continue
+        out[name] = e["hbm_bytes"]
+    return out
+
+
 # ------------------------------------------------------------------ main
 def main():
     ap = argparse.ArgumentParser()
@@ -209,7 +231,8 @@ def main():
     ap.add_argument("--only", default="all",
                     help="all | causal_prefill | window_sink | decode | block_sparse | copy (HBM counter calibration)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--traffic", default=None, help="JSON file with measured HBM bytes per launch of the prefill kernel")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="JSON file of HBM bytes per launch measured with rocprofv3 counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -269,10 +292,11 @@ def main():
     else:
         achieved = head["bytes_per_step"] / (head["launch_ms_mean"] * 1e-3) / 1e9
         peak, unit = PEAK_HBM_GBPS, "GB/s"
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        with open(args.traffic) as f:
-            traffic = json.load(f).get(head["workload"])
+    measured = load_traffic(args.traffic)
+    traffic = measured.get(head["workload"])
+    for r in also.values():
+        if r.get("workload") in measured:
+            r["hbm_bytes_per_launch_measured"] = measured[r["workload"]]
     line = {
         "metric": METRIC,
         "value": round(head["value"], 3),
