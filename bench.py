@@ -6,8 +6,9 @@ One step = one call of the hot path on one batch of synthetic input.  The headli
 also carries, under ``also``, the other workloads of the path measured the same way:
 sliding-window prefill with sinks (T = 32768, W = 1024), KV-cache decode (batch 64, cache
 lengths uniform in [1024, 32768]; decode KV-read GB/s), a 512-token chunk appended at each
-sequence's cache offset, and block-sparse prefill (T = 65536, block 128) with its block
-selection.
+sequence's cache offset, sliding-window decode over W = 1024-slot ring caches with the
+step's K/V appended (batch 64), and block-sparse prefill (T = 65536, block 128) with its
+block selection.
 
 Algorithmic work: prefill flops = 4 * head_dim * sum over heads of the allowed (row, key)
 pairs (QK^T and PV, 2 flops per multiply-add; masked halves of tiles and the softmax are not
@@ -35,7 +36,7 @@ sys.path.insert(0, ROOT)
 
 import synth  # noqa: E402
 from sparse_offset_causal_amd import (attn_block_select, attn_decode, attn_decode_workspace_bytes,  # noqa: E402
-                                      attn_prefill)
+                                      attn_prefill, attn_ring_decode, attn_ring_decode_workspace_bytes)
 
 METRIC = "prefill TFLOP/s + decode KV-read GB/s, offset-causal GQA attention, 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
@@ -150,6 +151,26 @@ def bench_decode_and_chunk(steps, warmup, B=64):
     return rd, rc
 
 
+def bench_ring_decode(steps, warmup, B=64, W=1024):
+    """Sliding-window decode over full W-slot ring caches (every sequence has seen more than
+    W tokens), the step's K/V appended by the call."""
+    Hq, Hkv, d = 32, 8, 128
+    st = synth.ring_state(B, Hq, Hkv, d, W, n_lo=W, n_hi=8 * W)
+    q, kn, vn = (t.to("cuda") for t in synth.ring_step(B, Hq, Hkv, d, 0))
+    k_ring, v_ring, n_seen, sink = st.k.to("cuda"), st.v.to("cuda"), st.n_seen.to("cuda"), st.sink.to("cuda")
+    o = torch.empty_like(q)
+    ws = torch.empty(attn_ring_decode_workspace_bytes(q, k_ring), dtype=torch.uint8, device="cuda")
+    fn = lambda: attn_ring_decode(q, kn, vn, k_ring, v_ring, n_seen, sink=sink, workspace=ws, out=o)
+    r = Timer(fn, steps, warmup).run()
+    kv_bytes = float(B * 2 * Hkv * W * d * 2)        # every filled slot's K and V row
+    other = float(2 * B * Hq * d * 2 + 2 * 2 * B * Hkv * d * 2)  # q, o; new K/V read and written
+    nbytes = kv_bytes + other
+    r.update(workload=f"ring_decode_bf16_B{B}_W{W}_{Hq}q{Hkv}kv_d{d}", bytes_per_step=nbytes,
+             value=nbytes / (r["ms_per_step"] * 1e-3) / 1e9, kernel_GBps=nbytes / (r["launch_ms_mean"] * 1e-3) / 1e9,
+             unit="GB/s")
+    return r
+
+
 def bench_block_sparse(steps, warmup, T=65536, BS=128):
     w = synth.block_sparse_prefill(T=T, BS=BS)
     q, k, v, _, _ = to_dev(w)
@@ -229,7 +250,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", default="all",
-                    help="all | causal_prefill | window_sink | decode | block_sparse | copy (HBM counter calibration)")
+                    help="all | causal_prefill | window_sink | decode | ring_decode | block_sparse | copy (HBM counter calibration)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="JSON file of HBM bytes per launch measured with rocprofv3 counters")
@@ -273,6 +294,11 @@ def main():
         also["decode"], also["chunk_prefill"] = rd, rc
         log(f"decode: {rd['value']:.0f} GB/s ({rd['ms_per_step']:.3f} ms); chunk: {rc['value']:.1f} TFLOP/s")
         torch.cuda.empty_cache()
+    if args.only in ("all", "ring_decode"):
+        r = bench_ring_decode(args.steps, args.warmup)
+        also["ring_decode"] = r
+        log(f"ring decode: {r['value']:.0f} GB/s ({r['ms_per_step']:.3f} ms)")
+        torch.cuda.empty_cache()
     if args.only in ("all", "block_sparse"):
         rs, rp = bench_block_sparse(args.steps, args.warmup)
         also["block_select"], also["block_sparse_prefill"] = rs, rp
@@ -281,7 +307,7 @@ def main():
         torch.cuda.empty_cache()
 
     if head is None:  # a single non-headline workload was requested: its main kernel heads the line
-        for key in ("window_sink_prefill", "decode", "block_sparse_prefill"):
+        for key in ("window_sink_prefill", "decode", "ring_decode", "block_sparse_prefill"):
             if key in also:
                 head = also[key]
                 break

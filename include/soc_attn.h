@@ -132,6 +132,40 @@ int attn_decode(const attn_shape_t* shape, const void* q, attn_strides_t q_strid
                 void* workspace, size_t workspace_bytes, int32_t split_tokens, hipStream_t stream);
 
 /*
+ * attn_ring_decode_workspace_bytes -- bytes of device workspace attn_ring_decode needs
+ * (split_tokens <= 0 selects the default split).  Returns 0 for an invalid shape.
+ */
+size_t attn_ring_decode_workspace_bytes(const attn_shape_t* shape, int32_t split_tokens);
+
+/*
+ * attn_ring_decode -- one decode step of sliding-window attention over a W-slot ring
+ * cache, appending the step's K/V itself (sotaaz.com/post/attention-in-code, section 2,
+ * the ring-buffer cache: token n's K/V go to slot n mod W over the oldest entry, and the
+ * step attends to the filled slots in any order, which a softmax cannot tell apart).
+ *
+ *  shape      tq = 1; tk = W, the ring's slots per (sequence, KV head).
+ *  q          [batch, n_heads, 1, head_dim]                 (dtype)
+ *  k_new, v_new [batch, n_kv, 1, head_dim], strides new_strides: the step's K/V rows.
+ *  k_ring, v_ring [batch, n_kv, W, head_dim], strides ring_strides; updated in place:
+ *             slot n_seen[b] % W of every KV head of sequence b receives k_new / v_new.
+ *  n_seen     device int32 [batch], >= 0: tokens of sequence b written to the ring
+ *             before this step.  Read only; the caller advances it after the step.
+ *  o          [batch, n_heads, 1, head_dim] output: attention of q over the
+ *             min(n_seen[b] + 1, W) filled slots, the new token included.  This equals
+ *             attn_prefill with window W at position n_seen[b] over the whole history.
+ *  sink, scale as attn_prefill (the sink joins the normaliser once per row).
+ *  workspace  at least attn_ring_decode_workspace_bytes(shape, split_tokens) bytes.
+ * A small append kernel writes the rows and the per-sequence count of filled slots; the
+ * split-KV decode and merge of attn_decode then run over the ring.  Same dtype and
+ * head_dim rules as attn_decode; bf16 needs n_heads / n_kv <= 32.
+ */
+int attn_ring_decode(const attn_shape_t* shape, const void* q, attn_strides_t q_strides, const void* k_new,
+                     const void* v_new, attn_strides_t new_strides, void* k_ring, void* v_ring,
+                     attn_strides_t ring_strides, void* o, attn_strides_t o_strides, const int32_t* n_seen,
+                     const float* sink, float scale, void* workspace, size_t workspace_bytes, int32_t split_tokens,
+                     hipStream_t stream);
+
+/*
  * attn_block_select_workspace_bytes -- device workspace for attn_block_select.
  */
 size_t attn_block_select_workspace_bytes(const attn_shape_t* shape, int32_t block_size);

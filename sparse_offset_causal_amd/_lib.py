@@ -14,6 +14,8 @@ EXPORTS = (
     "attn_prefill",
     "attn_decode_workspace_bytes",
     "attn_decode",
+    "attn_ring_decode_workspace_bytes",
+    "attn_ring_decode",
     "attn_block_select_workspace_bytes",
     "attn_block_select",
     "attn_block_list_from_mask",
@@ -51,6 +53,11 @@ def load() -> ctypes.CDLL:
     lib.attn_decode.argtypes = [POINTER(AttnShape), P, AttnStrides, P, P, AttnStrides, P, AttnStrides,
                                 P, c_int32, P, c_float, P, c_size_t, c_int32, P]
     lib.attn_decode.restype = c_int
+    lib.attn_ring_decode_workspace_bytes.argtypes = [POINTER(AttnShape), c_int32]
+    lib.attn_ring_decode_workspace_bytes.restype = c_size_t
+    lib.attn_ring_decode.argtypes = [POINTER(AttnShape), P, AttnStrides, P, P, AttnStrides, P, P, AttnStrides,
+                                     P, AttnStrides, P, P, c_float, P, c_size_t, c_int32, P]
+    lib.attn_ring_decode.restype = c_int
     lib.attn_block_select_workspace_bytes.argtypes = [POINTER(AttnShape), c_int32]
     lib.attn_block_select_workspace_bytes.restype = c_size_t
     lib.attn_block_select.argtypes = [POINTER(AttnShape), P, AttnStrides, P, AttnStrides, P, c_int32, c_int32,

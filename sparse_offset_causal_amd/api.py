@@ -129,6 +129,40 @@ def attn_decode(q, k, v, cache_off=None, window=0, sink=None, scale=None, split_
     return o
 
 
+def attn_ring_decode_workspace_bytes(q, k_ring, split_tokens=0) -> int:
+    return int(_lib.load().attn_ring_decode_workspace_bytes(_shape(q, k_ring), int(split_tokens)))
+
+
+def attn_ring_decode(q, k_new, v_new, k_ring, v_ring, n_seen, sink=None, scale=None, split_tokens=0,
+                     workspace=None, out=None):
+    """One sliding-window decode step over a W-slot ring cache (see attn_ring_decode in
+    include/soc_attn.h): writes k_new / v_new [B,Hkv,1,d] into slot n_seen[b] % W of k_ring / v_ring
+    [B,Hkv,W,d] (in place) and returns the attention of q [B,Hq,1,d] over the filled slots.  n_seen is
+    an int32 GPU tensor [B] the caller advances after the step."""
+    _common(q, k_ring, v_ring, None, sink)
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        _check4(name, t)
+        if t.dtype != q.dtype or t.shape != (k_ring.shape[0], k_ring.shape[1], 1, k_ring.shape[3]):
+            raise ValueError(f"{name} must be [B, Hkv, 1, d] in the ring's dtype")
+    if k_new.stride() != v_new.stride():
+        raise ValueError("k_new and v_new must share strides")
+    if (n_seen.dtype != torch.int32 or not n_seen.is_cuda or n_seen.numel() != q.shape[0] or
+            not n_seen.is_contiguous()):
+        raise ValueError("n_seen must be a contiguous int32 GPU tensor with one entry per sequence")
+    o = _out(q, out)
+    lib = _lib.load()
+    shape = _shape(q, k_ring)
+    need = int(lib.attn_ring_decode_workspace_bytes(shape, int(split_tokens)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    rc = lib.attn_ring_decode(shape, q.data_ptr(), _strides(q), k_new.data_ptr(), v_new.data_ptr(), _strides(k_new),
+                              k_ring.data_ptr(), v_ring.data_ptr(), _strides(k_ring), o.data_ptr(), _strides(o),
+                              n_seen.data_ptr(), _ptr(sink), float(scale or 0.0), workspace.data_ptr(),
+                              workspace.numel() * workspace.element_size(), int(split_tokens), _stream())
+    _check(rc)
+    return o
+
+
 def attn_block_select_workspace_bytes(q, k, block_size=128) -> int:
     return int(_lib.load().attn_block_select_workspace_bytes(_shape(q, k), int(block_size)))
 

@@ -257,6 +257,83 @@ int attn_decode(const attn_shape_t* shape, const void* q, attn_strides_t q_strid
   return finish(e, stream, "attn_decode merge launch");
 }
 
+size_t attn_ring_decode_workspace_bytes(const attn_shape_t* shape, int32_t split_tokens) {
+  if (check_shape(shape) != ATTN_OK) return 0;
+  return attn_decode_workspace_bytes(shape, split_tokens) + round_up(sizeof(int32_t) * shape->batch, 256);
+}
+
+int attn_ring_decode(const attn_shape_t* shape, const void* q, attn_strides_t q_strides, const void* k_new,
+                     const void* v_new, attn_strides_t new_strides, void* k_ring, void* v_ring,
+                     attn_strides_t ring_strides, void* o, attn_strides_t o_strides, const int32_t* n_seen,
+                     const float* sink, float scale, void* workspace, size_t workspace_bytes, int32_t split_tokens,
+                     hipStream_t stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if ((rc = check_attn_dtype(shape))) return rc;
+  if (shape->batch == 0) {
+    g_err.clear();
+    return ATTN_OK;
+  }
+  if (shape->tq != 1) return fail(ATTN_E_INVAL, "ring decode takes one query row per sequence (tq = 1)");
+  if ((rc = check_tensors(shape, q, q_strides, k_ring, v_ring, ring_strides, o, o_strides))) return rc;
+  if (!k_new || !v_new || !n_seen) return fail(ATTN_E_INVAL, "k_new, v_new and n_seen must be non-NULL device pointers");
+  const size_t esz = elem_size(shape->dtype);
+  if (!aligned16(k_new) || !aligned16(v_new)) return fail(ATTN_E_INVAL, "k_new and v_new must be 16-byte aligned");
+  if (!strides_ok(new_strides, esz)) return fail(ATTN_E_INVAL, "strides must be non-negative multiples of 16 bytes (in elements)");
+  if (shape->dtype == ATTN_BF16 && (int64_t)shape->tk * ring_strides.t * 2 > (int64_t)0xffffffff)
+    return fail(ATTN_E_UNSUPPORTED, "one (sequence, KV head) ring slice spans more than 4 GiB (W * slot stride)");
+  if (shape->dtype == ATTN_BF16 && shape->n_heads / shape->n_kv > 32)
+    return fail(ATTN_E_UNSUPPORTED, "bf16 decode serves at most 32 query rows per KV head (n_heads/n_kv <= 32)");
+  const int split = split_tokens > 0 ? split_tokens : default_split(shape);
+  const int64_t nsplit = (shape->tk + split - 1) / split;
+  const size_t part_bytes = attn_decode_workspace_bytes(shape, split);
+  const size_t need = attn_ring_decode_workspace_bytes(shape, split);
+  if (!workspace) return fail(ATTN_E_WORKSPACE, "workspace is NULL");
+  if (!aligned16(workspace)) return fail(ATTN_E_WORKSPACE, "workspace must be 16-byte aligned");
+  if (workspace_bytes < need)
+    return fail(ATTN_E_WORKSPACE, "workspace too small: need " + std::to_string(need) + " bytes");
+  if ((int64_t)shape->batch * shape->n_heads * nsplit >= (int64_t)1 << 31)
+    return fail(ATTN_E_INVAL, "problem too large for one grid");
+  if (debug_mode()) {
+    std::vector<int32_t> h(shape->batch);
+    hipError_t e = hipMemcpyAsync(h.data(), n_seen, sizeof(int32_t) * shape->batch, hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "ATTN_DEBUG: reading n_seen");
+    for (int b = 0; b < shape->batch; ++b)
+      if (h[b] < 0) return fail(ATTN_E_INVAL, "ATTN_DEBUG: n_seen[" + std::to_string(b) + "] is negative");
+  }
+
+  int32_t* offs = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + part_bytes);
+  soc::RingAppendArgs r{};
+  r.k_new = k_new;
+  r.v_new = v_new;
+  r.n_sb = new_strides.b;
+  r.n_sh = new_strides.h;
+  r.k_ring = k_ring;
+  r.v_ring = v_ring;
+  r.r_sb = ring_strides.b;
+  r.r_sh = ring_strides.h;
+  r.r_st = ring_strides.t;
+  r.n_seen = n_seen;
+  r.cache_off_out = offs;
+  r.B = shape->batch;
+  r.Hkv = shape->n_kv;
+  r.W = shape->tk;
+  r.esz = (int32_t)esz;
+  r.row_bytes = (int32_t)(shape->head_dim * esz);
+  hipError_t e = soc::launch_ring_append(r, stream);
+  if (e != hipSuccess) return hip_fail(e, "attn_ring_decode append launch");
+
+  soc::AttnArgs a = make_args(shape, q, q_strides, k_ring, v_ring, ring_strides, o, o_strides, offs, 0, sink, scale);
+  a.part = static_cast<float*>(workspace);
+  a.nsplit = (int32_t)nsplit;
+  a.split = split;
+  e = shape->dtype == ATTN_BF16 ? soc::launch_decode_bf16(a, stream) : soc::launch_decode_f32(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "attn_ring_decode split launch");
+  e = soc::launch_decode_merge(a, shape->dtype == ATTN_BF16, stream);
+  return finish(e, stream, "attn_ring_decode merge launch");
+}
+
 size_t attn_block_select_workspace_bytes(const attn_shape_t* shape, int32_t block_size) {
   if (check_shape(shape) != ATTN_OK || block_size < 1) return 0;
   return select_layout(shape, block_size).total;

@@ -69,6 +69,21 @@ struct SelectArgs {
   double* cand;        // workspace [B, Hq, nqb * nkb]  candidates of the order statistic
 };
 
+// One decode step's K/V rows into a W-slot ring cache (slot n_seen[b] % W) and the
+// per-sequence cache offset min(n_seen[b], W - 1) that the split-KV decode then uses.
+struct RingAppendArgs {
+  const void* k_new;
+  const void* v_new;
+  int64_t n_sb, n_sh;  // element strides of k_new / v_new (batch, head)
+  void* k_ring;
+  void* v_ring;
+  int64_t r_sb, r_sh, r_st;  // element strides of the rings (batch, head, slot)
+  const int32_t* n_seen;     // [B]
+  int32_t* cache_off_out;    // [B]
+  int32_t B, Hkv, W, row_bytes, esz;
+};
+
+hipError_t launch_ring_append(const RingAppendArgs& r, hipStream_t s);
 hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_prefill_f32(const AttnArgs& a, hipStream_t s);
 hipError_t launch_decode_bf16(const AttnArgs& a, hipStream_t s);

@@ -179,3 +179,37 @@ def block_sparse_prefill(T=65536, BS=128, Hq=32, Hkv=8, d=128, frac=0.05, norm_m
     w.keep_radius = keep_radius
     w.meta["planted"] = planted
     return w
+
+
+@dataclass
+class RingState:
+    """A W-slot ring cache per (sequence, KV head) and the per-sequence count of tokens
+    already written (n_seen).  Slots a sequence has not written yet (slot >= n_seen when
+    n_seen < W) hold large stale values that a correct reader never touches."""
+
+    k: torch.Tensor       # [B, Hkv, W, d]
+    v: torch.Tensor       # [B, Hkv, W, d]
+    n_seen: torch.Tensor  # [B] int32
+    sink: torch.Tensor    # [Hq] float32
+
+
+def ring_state(B=64, Hq=32, Hkv=8, d=128, W=1024, n_lo=0, n_hi=4096, seed=0, dtype=torch.bfloat16,
+               stale=1.0e4, n_seen=None) -> RingState:
+    """Ring contents N(0,1); n_seen uniform integers in [n_lo, n_hi] (or the given list);
+    sink N(0,1) per head."""
+    k = normal((B, Hkv, W, d), seed + SEED_K, torch.float32)
+    v = normal((B, Hkv, W, d), seed + SEED_V, torch.float32)
+    n = cache_lengths(B, n_lo, n_hi, seed) if n_seen is None else torch.tensor(n_seen, dtype=torch.int32)
+    for b in range(B):
+        if int(n[b]) < W:
+            k[b, :, int(n[b]):] = stale
+            v[b, :, int(n[b]):] = stale
+    sink = normal((Hq,), seed + SEED_SINK)
+    return RingState(k.to(dtype), v.to(dtype), n, sink)
+
+
+def ring_step(B, Hq, Hkv, d, step, seed=0, dtype=torch.bfloat16):
+    """One decode step's inputs: q [B, Hq, 1, d] and the new token's k, v [B, Hkv, 1, d]."""
+    base = seed + 1000 + 10 * step
+    return (normal((B, Hq, 1, d), base + SEED_Q, dtype), normal((B, Hkv, 1, d), base + SEED_K, dtype),
+            normal((B, Hkv, 1, d), base + SEED_V, dtype))

@@ -105,6 +105,29 @@ def test_decode_workspace_checks(lib):
     assert "too small" in _lib.last_error()
 
 
+def test_ring_decode_checks(lib):
+    shape = S(tq=1, tk=1024)
+    need = lib.attn_ring_decode_workspace_bytes(ctypes.byref(shape), 256)
+    assert need == lib.attn_decode_workspace_bytes(ctypes.byref(shape), 256) + 256
+    assert lib.attn_ring_decode_workspace_bytes(ctypes.byref(S(h=6, kv=4)), 0) == 0
+
+    def call(**kw):
+        sh = kw.get("shape", shape)
+        return lib.attn_ring_decode(ctypes.byref(sh), FAKE, st(tk=1), kw.get("kn", FAKE), FAKE, st(tk=1, h=2),
+                                    FAKE, FAKE, st(tk=1024, h=2), FAKE, st(tk=1), kw.get("ns", FAKE), None, 0.0,
+                                    kw.get("ws", FAKE), kw.get("wsb", need), 256, None)
+
+    assert call(shape=S(tq=2, tk=1024)) == ATTN_E_INVAL
+    assert "tq = 1" in _lib.last_error()
+    assert call(kn=None) == ATTN_E_INVAL
+    assert call(ns=None) == ATTN_E_INVAL
+    assert call(kn=FAKE + 4) == ATTN_E_INVAL
+    assert call(ws=None) == ATTN_E_WORKSPACE
+    assert call(wsb=need - 1) == ATTN_E_WORKSPACE
+    assert call(shape=S(d=64, tq=1, tk=1024)) == ATTN_E_UNSUPPORTED
+    assert call(shape=S(b=0, tq=1, tk=1024), kn=None, ns=None, ws=None) == 0
+
+
 def test_block_select_checks(lib):
     shape = S(tq=256, tk=256)
     need = lib.attn_block_select_workspace_bytes(ctypes.byref(shape), 128)
