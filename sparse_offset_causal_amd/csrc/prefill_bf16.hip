@@ -35,8 +35,10 @@
 //   plus immediates or one scalar per tile.
 //
 // Grid order: workgroup i runs on XCD i % 8.  When the number of KV groups (batch x n_kv)
-// is a multiple of 8, each XCD is given whole KV groups (their K/V stay in that XCD's L2),
-// and within an XCD the query tiles with the most keys are dispatched first.
+// is a multiple of 8, each XCD is given whole KV groups (their K/V stay in that XCD's L2);
+// within an XCD the workgroups of one KV group are dispatched together (all its query
+// tiles and heads, the query tiles with the most keys first), so they stream the group's
+// K/V tiles at about the same time.
 
 #include <type_traits>
 
@@ -62,12 +64,13 @@ typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
 __device__ __forceinline__ void map_block(int bid, const AttnArgs& a, int n_qt, int& qt, int& h, int& b) {
   const int units = a.B * a.Hkv;
   if ((units & 7) == 0) {
+    // unit-major within the XCD: all query tiles and heads of one KV group run together, so
+    // the group's K/V stream is fetched from HBM about once and re-read from L2
     const int xcd = bid & 7, j = bid >> 3;
-    const int upx = units >> 3;
-    const int per_row = upx * a.g;
-    const int qt_rev = j / per_row;
-    const int rem = j - qt_rev * per_row;
-    const int ul = rem / a.g, hg = rem - ul * a.g;
+    const int per_unit = n_qt * a.g;
+    const int ul = j / per_unit;
+    const int rem = j - ul * per_unit;
+    const int qt_rev = rem / a.g, hg = rem - qt_rev * a.g;
     const int unit = ul * 8 + xcd;
     b = unit / a.Hkv;
     const int kvh = unit - b * a.Hkv;
