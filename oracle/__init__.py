@@ -15,6 +15,8 @@ select  block selection by a mean-centroid score OR'd with a max-key-radius
         score, each with its own per-head order-statistic threshold, taken step
         by step.
 ring    a W-slot ring-buffer KV cache, an independent route to the window rule.
+mla     multi-head latent attention, plain (keys and values rebuilt per head) and
+        absorbed (query moved into latent space, one shared latent KV head).
 brute   pure-Python scalar loops for tiny shapes (a second, independent
         implementation of both definitions).
 

@@ -69,7 +69,8 @@ def attend(q, k, v, cache_off=None, window=0, sink=None, scale=None, block_mask=
            block_size=0, rows=None, heads=None, batches=None, row_block=1024, return_lse=False):
     """Masked attention, float64.
 
-    q: [B, Hq, Tq, d]; k, v: [B, Hkv, Tcap, d] (numpy or torch, any float dtype).
+    q: [B, Hq, Tq, d]; k: [B, Hkv, Tcap, d]; v: [B, Hkv, Tcap, dv] (numpy or torch, any
+    float dtype; dv = d except where the value width differs, as for latent attention).
     cache_off: int [B] or None (then off_b = Tcap - Tq).  Tk_b = off_b + Tq <= Tcap;
     rows of k/v at or beyond Tk_b are never read.
     block_mask: [B, Hq, ceil(Tq/bs), ceil(Tcap/bs)] (nonzero = kept) with bs =
@@ -77,7 +78,7 @@ def attend(q, k, v, cache_off=None, window=0, sink=None, scale=None, block_mask=
     j // bs (j is the absolute key index).
     rows / heads / batches: optional subsets to compute (default all).
 
-    Returns o [len(batches), len(heads), len(rows), d] float64, and with
+    Returns o [len(batches), len(heads), len(rows), dv] float64, and with
     ``return_lse`` also lse = log sum_{allowed j} exp(s_j) (no sink; -inf if empty).
     """
     # inputs are widened to float64 slice by slice (exact), so a large cache is never copied whole
@@ -96,7 +97,7 @@ def attend(q, k, v, cache_off=None, window=0, sink=None, scale=None, block_mask=
     heads = np.arange(Hq) if heads is None else np.asarray(heads, dtype=np.int64)
     batches = np.arange(B) if batches is None else np.asarray(batches, dtype=np.int64)
 
-    out = np.zeros((len(batches), len(heads), len(rows), d))
+    out = np.zeros((len(batches), len(heads), len(rows), v.shape[-1]))  # value width may differ from d
     lse = np.full((len(batches), len(heads), len(rows)), -np.inf)
     for bi, b in enumerate(batches):
         tkb = int(off[b]) + Tq
