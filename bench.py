@@ -7,8 +7,9 @@ also carries, under ``also``, the other workloads of the path measured the same 
 sliding-window prefill with sinks (T = 32768, W = 1024), KV-cache decode (batch 64, cache
 lengths uniform in [1024, 32768]; decode KV-read GB/s), a 512-token chunk appended at each
 sequence's cache offset, sliding-window decode over W = 1024-slot ring caches with the
-step's K/V appended (batch 64), and block-sparse prefill (T = 65536, block 128) with its
-block selection.
+step's K/V appended (batch 64), multi-head latent attention decode in absorbed form
+(batch 64, 16 heads, 576 numbers per cached token), and block-sparse prefill (T = 65536,
+block 128) with its block selection.
 
 Algorithmic work: prefill flops = 4 * head_dim * sum over heads of the allowed (row, key)
 pairs (QK^T and PV, 2 flops per multiply-add; masked halves of tiles and the softmax are not
@@ -36,7 +37,8 @@ sys.path.insert(0, ROOT)
 
 import synth  # noqa: E402
 from sparse_offset_causal_amd import (attn_block_select, attn_decode, attn_decode_workspace_bytes,  # noqa: E402
-                                      attn_prefill, attn_ring_decode, attn_ring_decode_workspace_bytes)
+                                      attn_mla_decode, attn_mla_decode_workspace_bytes, attn_prefill,
+                                      attn_ring_decode, attn_ring_decode_workspace_bytes)
 
 METRIC = "prefill TFLOP/s + decode KV-read GB/s, offset-causal GQA attention, 1 GPU"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
@@ -171,6 +173,27 @@ def bench_ring_decode(steps, warmup, B=64, W=1024):
     return r
 
 
+def bench_mla_decode(steps, warmup, B=64, H=16):
+    """Multi-head latent attention decode, absorbed form: batch 64, 16 heads, latent 512 +
+    rope 64 per cached token, cache lengths uniform in [1024, 32768]."""
+    m = synth.mla_cache(B=B, H=H)
+    qn, qr, ck, kr = m.q_nope.cuda(), m.q_rope.cuda(), m.c_kv.cuda(), m.k_rope.cuda()
+    wk, wv, off = m.w_uk.cuda(), m.w_uv.cuda(), m.cache_off.cuda()
+    o = torch.empty((B, H, 1, 128), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(attn_mla_decode_workspace_bytes(qn, qr, ck, kr, wv), dtype=torch.uint8, device="cuda")
+    fn = lambda: attn_mla_decode(qn, qr, ck, kr, wk, wv, cache_off=off, workspace=ws, out=o)
+    r = Timer(fn, steps, warmup).run()
+    L = m.cache_off.numpy().astype(np.int64)
+    lat_bytes = float(((L + 1) * (512 + 64) * 2).sum())  # every cached token's latent and rope key, once
+    other = float(B * H * (128 + 64 + 128) * 2 + 2 * H * 512 * 128 * 2)  # q, o, w_uk, w_uv
+    nbytes = lat_bytes + other
+    r.update(workload=f"mla_decode_bf16_B{B}_H{H}_cache1024-32768_r512_rope64", bytes_per_step=nbytes,
+             value=nbytes / (r["ms_per_step"] * 1e-3) / 1e9, kernel_GBps=nbytes / (r["launch_ms_mean"] * 1e-3) / 1e9,
+             unit="GB/s")
+    del ck, kr
+    return r
+
+
 def bench_block_sparse(steps, warmup, T=65536, BS=128):
     w = synth.block_sparse_prefill(T=T, BS=BS)
     q, k, v, _, _ = to_dev(w)
@@ -250,7 +273,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", default="all",
-                    help="all | causal_prefill | window_sink | decode | ring_decode | block_sparse | copy (HBM counter calibration)")
+                    help="all | causal_prefill | window_sink | decode | ring_decode | mla_decode | block_sparse | copy (HBM counter calibration)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="JSON file of HBM bytes per launch measured with rocprofv3 counters")
@@ -299,6 +322,11 @@ def main():
         also["ring_decode"] = r
         log(f"ring decode: {r['value']:.0f} GB/s ({r['ms_per_step']:.3f} ms)")
         torch.cuda.empty_cache()
+    if args.only in ("all", "mla_decode"):
+        r = bench_mla_decode(args.steps, args.warmup)
+        also["mla_decode"] = r
+        log(f"mla decode: {r['value']:.0f} GB/s ({r['ms_per_step']:.3f} ms)")
+        torch.cuda.empty_cache()
     if args.only in ("all", "block_sparse"):
         rs, rp = bench_block_sparse(args.steps, args.warmup)
         also["block_select"], also["block_sparse_prefill"] = rs, rp
@@ -307,7 +335,7 @@ def main():
         torch.cuda.empty_cache()
 
     if head is None:  # a single non-headline workload was requested: its main kernel heads the line
-        for key in ("window_sink_prefill", "decode", "ring_decode", "block_sparse_prefill"):
+        for key in ("window_sink_prefill", "decode", "ring_decode", "mla_decode", "block_sparse_prefill"):
             if key in also:
                 head = also[key]
                 break

@@ -166,6 +166,50 @@ int attn_ring_decode(const attn_shape_t* shape, const void* q, attn_strides_t q_
                      hipStream_t stream);
 
 /*
+ * Multi-head latent attention (sotaaz.com/post/attention-in-code, section 4).  The cache
+ * holds per token a latent c_kv of width kv_rank and one key k_rope of width rope_dim
+ * shared by all heads.  Head h's key is [c_kv @ w_uk[h], k_rope] and its value
+ * c_kv @ w_uv[h]; the query is [q_nope, q_rope].  Built: bf16, kv_rank 512, rope_dim 64,
+ * nope_dim 128, v_dim 128 (the DeepSeek-V2-Lite layout the page describes).
+ */
+typedef struct {
+  int32_t batch, n_heads, tq, tk; /* tk = cache rows addressable per sequence */
+  int32_t kv_rank, rope_dim, nope_dim, v_dim;
+  attn_dtype_t dtype;
+} attn_mla_shape_t;
+
+/*
+ * attn_mla_decode_workspace_bytes -- device workspace for attn_mla_decode (split_tokens
+ * <= 0 selects the default split).  Returns 0 for an invalid or unsupported shape.
+ */
+size_t attn_mla_decode_workspace_bytes(const attn_mla_shape_t* shape, int32_t split_tokens);
+
+/*
+ * attn_mla_decode -- MLA for a few query tokens per sequence against the latent cache,
+ * in absorbed form: no per-head key or value is built; each step reads kv_rank + rope_dim
+ * numbers per cached token, shared by all heads.
+ *
+ *  q_nope     [batch, n_heads, tq, nope_dim], q_rope [batch, n_heads, tq, rope_dim]
+ *  c_kv       [batch, tk, kv_rank], k_rope [batch, tk, rope_dim]: strides in elements with
+ *             .b (sequence) and .t (token); .h is ignored.  May be views of one
+ *             [batch, tk, kv_rank + rope_dim] buffer.
+ *  w_uk       [n_heads, kv_rank, nope_dim], w_uv [n_heads, kv_rank, v_dim], contiguous
+ *  o          [batch, n_heads, tq, v_dim] output
+ *  cache_off  device int32 [batch] or NULL (off_b = tk - tq): query token t of sequence b
+ *             sits at position off_b + t and sees cached tokens j <= off_b + t.
+ *  scale      <= 0 means 1/sqrt(nope_dim + rope_dim).
+ *  workspace  at least attn_mla_decode_workspace_bytes(shape, split_tokens) bytes.
+ *  Steps: q_lat = w_uk[h] q_nope (rounded to bf16); split-KV attention of [q_lat, q_rope]
+ *  over [c_kv, k_rope] averaging c_kv, in fp32; log-sum-exp merge; o = w_uv[h]^T o_lat.
+ *  At most 256 splits per sequence (ceil(tk / split_tokens) <= 256).
+ */
+int attn_mla_decode(const attn_mla_shape_t* shape, const void* q_nope, attn_strides_t qn_strides,
+                    const void* q_rope, attn_strides_t qr_strides, const void* c_kv, attn_strides_t ckv_strides,
+                    const void* k_rope, attn_strides_t kr_strides, const void* w_uk, const void* w_uv, void* o,
+                    attn_strides_t o_strides, const int32_t* cache_off, float scale, void* workspace,
+                    size_t workspace_bytes, int32_t split_tokens, hipStream_t stream);
+
+/*
  * attn_block_select_workspace_bytes -- device workspace for attn_block_select.
  */
 size_t attn_block_select_workspace_bytes(const attn_shape_t* shape, int32_t block_size);

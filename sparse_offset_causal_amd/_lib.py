@@ -16,6 +16,8 @@ EXPORTS = (
     "attn_decode",
     "attn_ring_decode_workspace_bytes",
     "attn_ring_decode",
+    "attn_mla_decode_workspace_bytes",
+    "attn_mla_decode",
     "attn_block_select_workspace_bytes",
     "attn_block_select",
     "attn_block_list_from_mask",
@@ -30,6 +32,12 @@ class AttnStrides(ctypes.Structure):
 class AttnShape(ctypes.Structure):
     _fields_ = [("batch", c_int32), ("n_heads", c_int32), ("n_kv", c_int32), ("head_dim", c_int32),
                 ("tq", c_int32), ("tk", c_int32), ("dtype", c_int)]
+
+
+class AttnMlaShape(ctypes.Structure):
+    _fields_ = [("batch", c_int32), ("n_heads", c_int32), ("tq", c_int32), ("tk", c_int32),
+                ("kv_rank", c_int32), ("rope_dim", c_int32), ("nope_dim", c_int32), ("v_dim", c_int32),
+                ("dtype", c_int)]
 
 
 _lib = None
@@ -58,6 +66,11 @@ def load() -> ctypes.CDLL:
     lib.attn_ring_decode.argtypes = [POINTER(AttnShape), P, AttnStrides, P, P, AttnStrides, P, P, AttnStrides,
                                      P, AttnStrides, P, P, c_float, P, c_size_t, c_int32, P]
     lib.attn_ring_decode.restype = c_int
+    lib.attn_mla_decode_workspace_bytes.argtypes = [POINTER(AttnMlaShape), c_int32]
+    lib.attn_mla_decode_workspace_bytes.restype = c_size_t
+    lib.attn_mla_decode.argtypes = [POINTER(AttnMlaShape), P, AttnStrides, P, AttnStrides, P, AttnStrides, P,
+                                    AttnStrides, P, P, P, AttnStrides, P, c_float, P, c_size_t, c_int32, P]
+    lib.attn_mla_decode.restype = c_int
     lib.attn_block_select_workspace_bytes.argtypes = [POINTER(AttnShape), c_int32]
     lib.attn_block_select_workspace_bytes.restype = c_size_t
     lib.attn_block_select.argtypes = [POINTER(AttnShape), P, AttnStrides, P, AttnStrides, P, c_int32, c_int32,
@@ -75,6 +88,6 @@ def last_error() -> str:
     return load().attn_last_error().decode()
 
 
-__all__ = ["AttnShape", "AttnStrides", "load", "last_error", "EXPORTS", "LIB_PATH", "ATTN_BF16", "ATTN_F32",
+__all__ = ["AttnShape", "AttnMlaShape", "AttnStrides", "load", "last_error", "EXPORTS", "LIB_PATH", "ATTN_BF16", "ATTN_F32",
            "ATTN_OK", "ATTN_E_INVAL", "ATTN_E_UNSUPPORTED", "ATTN_E_WORKSPACE", "ATTN_E_HIP",
            "c_uint8", "c_double"]

@@ -13,7 +13,7 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import AttnShape, AttnStrides
+from ._lib import AttnMlaShape, AttnShape, AttnStrides
 
 
 class AttnError(RuntimeError):
@@ -161,6 +161,53 @@ def attn_ring_decode(q, k_new, v_new, k_ring, v_ring, n_seen, sink=None, scale=N
                               workspace.numel() * workspace.element_size(), int(split_tokens), _stream())
     _check(rc)
     return o
+
+
+def _mla_shape(q_nope, q_rope, c_kv, k_rope, w_uv):
+    B, H, Tq, dn = q_nope.shape
+    return AttnMlaShape(B, H, Tq, c_kv.shape[1], c_kv.shape[2], q_rope.shape[3], dn, w_uv.shape[2],
+                        _dtype_code(q_nope))
+
+
+def attn_mla_decode_workspace_bytes(q_nope, q_rope, c_kv, k_rope, w_uv, split_tokens=0) -> int:
+    return int(_lib.load().attn_mla_decode_workspace_bytes(_mla_shape(q_nope, q_rope, c_kv, k_rope, w_uv),
+                                                           int(split_tokens)))
+
+
+def attn_mla_decode(q_nope, q_rope, c_kv, k_rope, w_uk, w_uv, cache_off=None, scale=None, split_tokens=0,
+                    workspace=None, out=None):
+    """Multi-head latent attention decode in absorbed form (see attn_mla_decode in include/soc_attn.h).
+    q_nope [B,H,Tq,128], q_rope [B,H,Tq,64], c_kv [B,Tk,512], k_rope [B,Tk,64] (token axis strided,
+    last axis contiguous), w_uk [H,512,128], w_uv [H,512,128] contiguous; returns o [B,H,Tq,128]."""
+    _check4("q_nope", q_nope)
+    _check4("q_rope", q_rope)
+    for name, t in (("c_kv", c_kv), ("k_rope", k_rope)):
+        if t.dim() != 3 or not t.is_cuda or t.stride(2) != 1:
+            raise ValueError(f"{name} must be a 3-D GPU tensor [batch, tokens, width] with a contiguous last axis")
+    for name, t in (("w_uk", w_uk), ("w_uv", w_uv)):
+        if t.dim() != 3 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 3-D GPU tensor [heads, kv_rank, width]")
+    if len({t.dtype for t in (q_nope, q_rope, c_kv, k_rope, w_uk, w_uv)}) != 1:
+        raise ValueError("all MLA inputs must share one dtype")
+    if cache_off is not None and (cache_off.dtype != torch.int32 or not cache_off.is_cuda or
+                                  cache_off.numel() != q_nope.shape[0] or not cache_off.is_contiguous()):
+        raise ValueError("cache_off must be a contiguous int32 GPU tensor with one entry per sequence")
+    B, H, Tq, _ = q_nope.shape
+    if out is None:
+        out = torch.empty((B, H, Tq, w_uv.shape[2]), dtype=q_nope.dtype, device=q_nope.device)
+    lib = _lib.load()
+    shape = _mla_shape(q_nope, q_rope, c_kv, k_rope, w_uv)
+    need = int(lib.attn_mla_decode_workspace_bytes(shape, int(split_tokens)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q_nope.device)
+    bt = lambda t: AttnStrides(t.stride(0), 0, t.stride(1))
+    rc = lib.attn_mla_decode(shape, q_nope.data_ptr(), _strides(q_nope), q_rope.data_ptr(), _strides(q_rope),
+                             c_kv.data_ptr(), bt(c_kv), k_rope.data_ptr(), bt(k_rope), w_uk.data_ptr(),
+                             w_uv.data_ptr(), out.data_ptr(), _strides(out), _ptr(cache_off), float(scale or 0.0),
+                             workspace.data_ptr(), workspace.numel() * workspace.element_size(), int(split_tokens),
+                             _stream())
+    _check(rc)
+    return out
 
 
 def attn_block_select_workspace_bytes(q, k, block_size=128) -> int:

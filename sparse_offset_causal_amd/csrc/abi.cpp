@@ -172,6 +172,63 @@ SelectLayout select_layout(const attn_shape_t* s, int bs) {
   return L;
 }
 
+int check_mla_shape(const attn_mla_shape_t* s) {
+  if (!s) return fail(ATTN_E_INVAL, "shape is NULL");
+  if (s->batch < 0 || s->n_heads < 1 || s->tq < 0 || s->tk < 0)
+    return fail(ATTN_E_INVAL, "batch, tq, tk must be >= 0 and n_heads >= 1");
+  if (s->tq > s->tk) return fail(ATTN_E_INVAL, "tq > tk: the query tokens must already be in the cache");
+  if (s->dtype != ATTN_BF16 || s->kv_rank != soc::kMlaRank || s->rope_dim != soc::kMlaRope ||
+      s->nope_dim != soc::kMlaNope || s->v_dim != soc::kMlaV)
+    return fail(ATTN_E_UNSUPPORTED, "MLA decode is built for bf16 with kv_rank 512, rope_dim 64, nope_dim 128, v_dim 128");
+  return ATTN_OK;
+}
+
+int mla_default_split(const attn_mla_shape_t* s) {
+  // work items of 512 tokens keep the persistent split waves' tail short; longer splits only
+  // where 256 per sequence would not cover the cache
+  int split = 512;
+  while ((int64_t)(s->tk + split - 1) / split > soc::kMlaMaxSplits) split *= 2;
+  return split;
+}
+
+int device_cus() {
+  static thread_local int cached_dev = -1, cached_cus = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev != cached_dev) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached_dev = dev;
+    cached_cus = n;
+  }
+  return cached_cus;
+}
+
+struct MlaLayout {
+  size_t q_lat, part_o, part_ml, o_lat, queue, total;
+  int split, nsplit;
+};
+
+MlaLayout mla_layout(const attn_mla_shape_t* s, int32_t split_tokens) {
+  MlaLayout L{};
+  L.split = split_tokens > 0 ? split_tokens : mla_default_split(s);
+  L.nsplit = s->tk > 0 ? (s->tk + L.split - 1) / L.split : 1;
+  const size_t rows = (size_t)s->batch * s->n_heads * s->tq;
+  size_t off = 0;
+  L.q_lat = off;
+  off = round_up(off + rows * soc::kMlaRank * 2, 256);
+  L.part_o = off;
+  off = round_up(off + rows * L.nsplit * soc::kMlaRank * sizeof(float), 256);
+  L.part_ml = off;
+  off = round_up(off + rows * L.nsplit * 2 * sizeof(float), 256);
+  L.o_lat = off;
+  off = round_up(off + rows * soc::kMlaRank * sizeof(float), 256);
+  L.queue = off;
+  off = round_up(off + sizeof(uint32_t), 256);
+  L.total = off;
+  return L;
+}
+
 }  // namespace
 
 extern "C" {
@@ -332,6 +389,80 @@ int attn_ring_decode(const attn_shape_t* shape, const void* q, attn_strides_t q_
   if (e != hipSuccess) return hip_fail(e, "attn_ring_decode split launch");
   e = soc::launch_decode_merge(a, shape->dtype == ATTN_BF16, stream);
   return finish(e, stream, "attn_ring_decode merge launch");
+}
+
+size_t attn_mla_decode_workspace_bytes(const attn_mla_shape_t* shape, int32_t split_tokens) {
+  if (check_mla_shape(shape) != ATTN_OK) return 0;
+  return mla_layout(shape, split_tokens).total;
+}
+
+int attn_mla_decode(const attn_mla_shape_t* shape, const void* q_nope, attn_strides_t qn_strides,
+                    const void* q_rope, attn_strides_t qr_strides, const void* c_kv, attn_strides_t ckv_strides,
+                    const void* k_rope, attn_strides_t kr_strides, const void* w_uk, const void* w_uv, void* o,
+                    attn_strides_t o_strides, const int32_t* cache_off, float scale, void* workspace,
+                    size_t workspace_bytes, int32_t split_tokens, hipStream_t stream) {
+  int rc = check_mla_shape(shape);
+  if (rc) return rc;
+  if (shape->tq == 0 || shape->batch == 0) {
+    g_err.clear();
+    return ATTN_OK;
+  }
+  if (!q_nope || !q_rope || !c_kv || !k_rope || !w_uk || !w_uv || !o)
+    return fail(ATTN_E_INVAL, "q_nope, q_rope, c_kv, k_rope, w_uk, w_uv and o must be non-NULL device pointers");
+  if (!aligned16(q_nope) || !aligned16(q_rope) || !aligned16(c_kv) || !aligned16(k_rope) || !aligned16(w_uk) ||
+      !aligned16(w_uv) || !aligned16(o))
+    return fail(ATTN_E_INVAL, "all tensors must be 16-byte aligned");
+  const attn_strides_t ckv_bt{ckv_strides.b, 0, ckv_strides.t}, kr_bt{kr_strides.b, 0, kr_strides.t};
+  if (!strides_ok(qn_strides, 2) || !strides_ok(qr_strides, 2) || !strides_ok(ckv_bt, 2) || !strides_ok(kr_bt, 2) ||
+      !strides_ok(o_strides, 2))
+    return fail(ATTN_E_INVAL, "strides must be non-negative multiples of 16 bytes (in elements)");
+  if (ckv_strides.t < soc::kMlaRank || kr_strides.t < soc::kMlaRope)
+    return fail(ATTN_E_INVAL, "c_kv / k_rope token strides must be at least kv_rank / rope_dim");
+  if ((int64_t)shape->tk * ckv_strides.t * 2 > (int64_t)0x7fffffff || (int64_t)shape->tk * kr_strides.t * 2 > (int64_t)0x7fffffff)
+    return fail(ATTN_E_UNSUPPORTED, "one sequence's latent cache spans more than 2 GiB");
+  const MlaLayout L = mla_layout(shape, split_tokens);
+  if (L.nsplit > soc::kMlaMaxSplits)
+    return fail(ATTN_E_INVAL, "more than 256 splits per sequence: raise split_tokens");
+  if (!workspace) return fail(ATTN_E_WORKSPACE, "workspace is NULL");
+  if (!aligned16(workspace)) return fail(ATTN_E_WORKSPACE, "workspace must be 16-byte aligned");
+  if (workspace_bytes < L.total)
+    return fail(ATTN_E_WORKSPACE, "workspace too small: need " + std::to_string(L.total) + " bytes");
+  const int64_t nrg = ((int64_t)shape->n_heads * shape->tq + 15) / 16;
+  if ((int64_t)shape->batch * nrg * L.nsplit >= (int64_t)1 << 31) return fail(ATTN_E_INVAL, "problem too large for one grid");
+  {
+    attn_shape_t s2{shape->batch, 1, 1, 128, shape->tq, shape->tk, ATTN_BF16};
+    if ((rc = check_offsets_debug(&s2, cache_off, stream))) return rc;
+  }
+  soc::MlaArgs a{};
+  a.q_nope = q_nope;
+  a.qn_sb = qn_strides.b; a.qn_sh = qn_strides.h; a.qn_st = qn_strides.t;
+  a.q_rope = q_rope;
+  a.qr_sb = qr_strides.b; a.qr_sh = qr_strides.h; a.qr_st = qr_strides.t;
+  a.c_kv = c_kv;
+  a.c_sb = ckv_strides.b; a.c_st = ckv_strides.t;
+  a.k_rope = k_rope;
+  a.r_sb = kr_strides.b; a.r_st = kr_strides.t;
+  a.w_uk = w_uk;
+  a.w_uv = w_uv;
+  a.o = o;
+  a.o_sb = o_strides.b; a.o_sh = o_strides.h; a.o_st = o_strides.t;
+  a.cache_off = cache_off;
+  a.B = shape->batch;
+  a.H = shape->n_heads;
+  a.tq = shape->tq;
+  a.tk = shape->tk;
+  const float sc = scale > 0.f ? scale : 1.f / std::sqrt((float)(shape->nope_dim + shape->rope_dim));
+  a.scale_log2 = sc * soc::kLog2e;
+  char* ws = static_cast<char*>(workspace);
+  a.q_lat = ws + L.q_lat;
+  a.part_o = reinterpret_cast<float*>(ws + L.part_o);
+  a.part_ml = reinterpret_cast<float*>(ws + L.part_ml);
+  a.o_lat = reinterpret_cast<float*>(ws + L.o_lat);
+  a.queue = reinterpret_cast<uint32_t*>(ws + L.queue);
+  a.nsplit = L.nsplit;
+  a.split = L.split;
+  a.n_waves = 2 * device_cus();  // the split kernel's LDS use allows two waves per CU
+  return finish(soc::launch_mla_decode(a, stream), stream, "attn_mla_decode launch");
 }
 
 size_t attn_block_select_workspace_bytes(const attn_shape_t* shape, int32_t block_size) {

@@ -84,6 +84,36 @@ struct RingAppendArgs {
 };
 
 hipError_t launch_ring_append(const RingAppendArgs& r, hipStream_t s);
+
+// Multi-head latent attention decode (bf16; latent width 512, rope width 64, per-head
+// query/key width 128 and value width 128).  Rows rho = h * tq + t of sequence b.
+constexpr int kMlaRank = 512, kMlaRope = 64, kMlaNope = 128, kMlaV = 128;
+struct MlaArgs {
+  const void* q_nope;
+  int64_t qn_sb, qn_sh, qn_st;
+  const void* q_rope;
+  int64_t qr_sb, qr_sh, qr_st;
+  const void* c_kv;
+  int64_t c_sb, c_st;
+  const void* k_rope;
+  int64_t r_sb, r_st;
+  const void* w_uk;  // [H, 512, 128]
+  const void* w_uv;  // [H, 512, 128]
+  void* o;
+  int64_t o_sb, o_sh, o_st;
+  const int32_t* cache_off;
+  int32_t B, H, tq, tk;
+  float scale_log2;
+  void* q_lat;      // workspace bf16 [B, H*tq, 512]
+  float* part_o;    // workspace f32 [B*H*tq, nsplit, 512]
+  float* part_ml;   // workspace f32 [B*H*tq, nsplit, 2]
+  float* o_lat;     // workspace f32 [B*H*tq, 512]  merged latent outputs
+  uint32_t* queue;  // workspace: next work item of the split kernel (cleared by the absorb kernel)
+  int32_t nsplit, split;
+  int32_t n_waves;  // persistent split waves
+};
+constexpr int kMlaMaxSplits = 256;  // splits per sequence the merge accepts
+hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t s);
 hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_prefill_f32(const AttnArgs& a, hipStream_t s);
 hipError_t launch_decode_bf16(const AttnArgs& a, hipStream_t s);

@@ -1,0 +1,385 @@
+// Multi-head latent attention decode for gfx950 (bf16 in, fp32 accumulate).
+//
+// The cache holds, per token, a latent c_kv (512 wide) and one rope key k_rope (64 wide)
+// shared by every head; head h's key is [c_kv @ w_uk[h], k_rope] and its value
+// c_kv @ w_uv[h] (sotaaz.com/post/attention-in-code, section 4).  Decode never builds those:
+// the query is folded into latent space once (q_lat = w_uk[h] q_nope), scores are
+// q_lat . c_kv + q_rope . k_rope, the softmax average is taken over the latents, and w_uv
+// is applied once per row to the averaged latent.  So a step reads 576 numbers per cached
+// token, shared by all heads.
+//
+//   mla_absorb_q_kernel     q_lat^T = w_uk[h] q_nope^T for 16 query rows of one head per wave
+//                           (v_mfma_f32_16x16x32_bf16, rounded to bf16); also clears the work
+//                           queue of the split pass
+//   mla_split_kernel        persistent 4-wave workgroups (two per CU: the LDS ring allows two)
+//                           that take (sequence, group of 16 query rows, split of keys) items
+//                           from an atomic queue; the 16 rows (heads x query tokens) are the N
+//                           columns of the MFMAs.  The four waves share the ring: each loads a
+//                           quarter of every block, computes the (cheap) scores in full and
+//                           a quarter of the 512-dim latent output.  Latent rows stream HBM -> LDS (buffer loads with the
+//                           LDS bit, 16-key blocks, a 4-stage ring, 16-byte chunks XOR-swizzled
+//                           by key); S^T = [C, R] [q_lat, q_rope]^T with
+//                           v_mfma_f32_16x16x32_bf16 over 576 dims; online softmax in the log2
+//                           domain; O^T += C^T P^T with v_mfma_f32_16x16x16bf16_1k, C read
+//                           transposed by ds_read_b64_tr_b16.  Each item's unnormalised
+//                           (max, sum, latent O) goes to the workspace.
+//   mla_merge_kernel        log-sum-exp merge of a row's splits into its latent output (fp32)
+//   mla_expand_kernel       o = w_uv[h]^T o_lat for 16 rows and 32 output dims of one head per
+//                           workgroup, rounded to bf16
+
+#include <type_traits>
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace soc {
+namespace {
+
+constexpr int MR = kMlaRank, MDR = kMlaRope, MDN = kMlaNope, MDV = kMlaV;
+constexpr int MKB = 16;                      // keys per block
+constexpr int MNST = 4;                      // ring stages (3 blocks in flight)
+constexpr int LAT_STAGE = MKB * MR;          // latent elements of one stage (16 KB)
+constexpr int ROPE_STAGE = MKB * MDR;        // rope elements of one stage (2 KB)
+constexpr int MSTAGE = LAT_STAGE + ROPE_STAGE;
+
+typedef short s16x4 __attribute__((__vector_size__(8)));
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
+
+__device__ __forceinline__ f32x4 mfma16k32(bf16x8 a, bf16x8 b, f32x4 c) {
+  // lane l: A[l%16][8(l/16)+e], B[8(l/16)+e][l%16], D[4(l/16)+v][l%16]
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16k16(bf16x4 a, bf16x4 b, f32x4 c) {
+  // lane l: A[l%16][4(l/16)+e], B[4(l/16)+e][l%16], D[4(l/16)+v][l%16]
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------------------
+// q_lat^T [512 x 16 rows] = w_uk[h] [512 x 128] q_nope^T [128 x 16 rows], one wave per
+// (head, 16 rows (b, t), 64 of the 512 latent dims); lane l: A = w_uk rows 16mb + l%16, B = row l%16 of q_nope,
+// D = q_lat dims 16mb + 4(l/16) + v of row l%16.
+__global__ void __launch_bounds__(64) mla_absorb_q_kernel(MlaArgs a) {
+  const int lane = threadIdx.x, G = lane >> 4, i16 = lane & 15;
+  if (blockIdx.x == 0 && lane == 0) *a.queue = 0u;  // work queue of the split pass
+  const int part = blockIdx.x & 7;  // 64 latent dims per wave
+  const int h = (blockIdx.x >> 3) % a.H;
+  const int grp = (blockIdx.x >> 3) / a.H;
+  const int nrow = a.B * a.tq;
+  const int idx = grp * 16 + i16;
+  const bool ok = idx < nrow;
+  const int b = ok ? idx / a.tq : 0, t = ok ? idx % a.tq : 0;
+  const bf16_t* qn = (const bf16_t*)a.q_nope + b * a.qn_sb + h * a.qn_sh + t * a.qn_st;
+  bf16x8 qb[4];
+  const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) qb[ks] = ok ? *(const bf16x8*)(qn + 32 * ks + 8 * G) : as_bf16x8(z);
+  const bf16_t* wk = (const bf16_t*)a.w_uk + (int64_t)h * MR * MDN;
+  const int R = a.H * a.tq;
+  bf16_t* out = (bf16_t*)a.q_lat + ((int64_t)b * R + h * a.tq + t) * MR;
+#pragma unroll
+  for (int mb = 4 * part; mb < 4 * part + 4; ++mb) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      acc = mfma16k32(*(const bf16x8*)(wk + (int64_t)(16 * mb + i16) * MDN + 32 * ks + 8 * G), qb[ks], acc);
+    if (ok) {
+      bf16x4 w;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) w[v] = (bf16_t)acc[v];
+      *(bf16x4*)(out + 16 * mb + 4 * G) = w;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Loads per wave per block: 4 latent rows (1 KB each) and a quarter (512 B) of the rope tile.
+constexpr int WAVE_LOADS = 5;
+template <int AFTER>
+__device__ __forceinline__ void wait_wave_blocks() {
+  static_assert(AFTER * WAVE_LOADS <= 63, "vmcnt counts at most 63 loads");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(AFTER * WAVE_LOADS) : "memory");
+}
+
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) mla_split_kernel(MlaArgs a) {
+  __shared__ __attribute__((aligned(1024))) bf16_t lds[MNST * MSTAGE];
+  __shared__ uint32_t item_sh;
+
+  const int tid = threadIdx.x, lane = tid & 63, G = lane >> 4, i16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int R = a.H * a.tq;
+  const int nrg = (R + 15) / 16;
+  const uint32_t n_items = (uint32_t)a.B * nrg * a.nsplit;
+
+  // fixed per-lane LDS element offsets
+  //   S A operand (key i16 of the block, chunk 4ks + G): i16*512 + ((4ks + G) ^ i16) * 8
+  //   rope A operand (key i16, chunk 4kr + G):          i16*64 + ((4kr + G) ^ (i16 & 7)) * 8
+  //   PV A operand, ds_read_b64_tr_b16 (lane j of group G: key 4G + j/4, dims 16db + 4(j%4)..+3):
+  //   with db = 8u + w this wave's dim blocks are u = wave, offset trb[w] + wave*128
+  int lat_s[16], rope_s[2], trb[8];
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks) lat_s[ks] = i16 * 512 + (((4 * ks + G) ^ i16) << 3);
+#pragma unroll
+  for (int kr = 0; kr < 2; ++kr) rope_s[kr] = i16 * 64 + (((4 * kr + G) ^ (i16 & 7)) << 3);
+  {
+    const int kk = 4 * G + (i16 >> 2);
+    const int x = (i16 & 3) >> 1;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) trb[w] = kk * 512 + ((((2 * w + x) ^ kk)) << 3) + 4 * (i16 & 1) + wave * 128;
+  }
+  // DMA lane offsets: latent row of key i goes to LDS row i (1 KB), LDS chunk j holding the
+  // row's chunk j ^ i; the rope tile holds key k's chunk j ^ (k & 7) at chunk j.  Wave w loads
+  // latent rows 4w..4w+3 and rope keys 4w..4w+3 (lanes 0..31).
+  const uint32_t rope_key = 4u * wave + (uint32_t)(lane >> 3);
+  const float c = a.scale_log2;
+
+  for (;;) {
+    __syncthreads();  // every wave is done with the previous item's LDS and item_sh
+    if (tid == 0) item_sh = atomicAdd(a.queue, 1u);
+    __syncthreads();
+    const uint32_t item = __builtin_amdgcn_readfirstlane(item_sh);
+    if (item >= n_items) break;
+    const int s = (int)(item % (uint32_t)a.nsplit);
+    const int rg = (int)((item / (uint32_t)a.nsplit) % (uint32_t)nrg);
+    const int b = (int)(item / ((uint32_t)a.nsplit * nrg));
+    const int off = __builtin_amdgcn_readfirstlane(a.cache_off ? a.cache_off[b] : a.tk - a.tq);
+    const int tkb = off + a.tq;
+    const int nsb = (tkb + a.split - 1) / a.split;
+    if (s >= nsb) continue;  // the merge reads only splits below nsb
+    const int ks0 = s * a.split, ks1 = min(ks0 + a.split, tkb);
+    const int nblk = (ks1 - ks0 + MKB - 1) / MKB;
+
+    // this lane's query row (MFMA column)
+    const int rho = rg * 16 + i16;
+    const bool row_ok = rho < R;
+    const int h = row_ok ? rho / a.tq : 0, t = row_ok ? rho % a.tq : 0;
+    const int pos = row_ok ? off + t : -1;
+
+    // latent and rope rows of this sequence; rows at or beyond the split's end read as zero
+    const uint32_t crow = (uint32_t)a.c_st * 2u, rrow = (uint32_t)a.r_st * 2u;
+    const bf16_t* cb = (const bf16_t*)a.c_kv + b * a.c_sb;
+    const bf16_t* rb = (const bf16_t*)a.k_rope + b * a.r_sb;
+    const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc((void*)cb, (short)0, (int)(ks1 * crow), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rrs = __builtin_amdgcn_make_buffer_rsrc((void*)rb, (short)0, (int)(ks1 * rrow), 0x00020000);
+    const uint32_t rope_v = rope_key * rrow + (uint32_t)(((lane & 7) ^ (rope_key & 7)) << 4);
+    auto issue = [&](int n, auto stage_tag) __attribute__((always_inline)) {
+      constexpr int ST = decltype(stage_tag)::value;
+      const uint32_t k0 = (uint32_t)(ks0 + n * MKB);
+      bf16_t* lat = lds + ST * MSTAGE;
+      bf16_t* rop = lat + LAT_STAGE;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = 4 * wave + i;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(crs, (lds_void_ptr)(lat + key * 512), 16,
+                                                 (uint32_t)((lane ^ key) << 4), (k0 + key) * crow, 0, 0);
+      }
+      if (lane < 32)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rrs, (lds_void_ptr)(rop + wave * 256), 16, rope_v, k0 * rrow, 0, 0);
+    };
+
+    // query fragments (B operand of S^T): dims 32ks + 8G .. +7 of row rho; 16 latent steps, 2 rope steps
+    bf16x8 qf[18];
+    {
+      const bf16_t* ql = (const bf16_t*)a.q_lat + ((int64_t)b * R + rho) * MR;
+      const bf16_t* qr = (const bf16_t*)a.q_rope + b * a.qr_sb + h * a.qr_sh + t * a.qr_st;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) qf[ks] = row_ok ? *(const bf16x8*)(ql + 32 * ks + 8 * G) : as_bf16x8(z);
+#pragma unroll
+      for (int kr = 0; kr < 2; ++kr) qf[16 + kr] = row_ok ? *(const bf16x8*)(qr + 32 * kr + 8 * G) : as_bf16x8(z);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // only block loads are counted below
+
+    if (nblk > 0) issue(0, std::integral_constant<int, 0>{});
+    if (nblk > 1) issue(1, std::integral_constant<int, 1>{});
+    if (nblk > 2) issue(2, std::integral_constant<int, 2>{});
+
+    f32x4 oacc[8];
+#pragma unroll
+    for (int d = 0; d < 8; ++d) oacc[d] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    float m_run = SOC_NEG_INF, l_run = 0.f;
+
+    auto step = [&](int n, auto stage_tag) __attribute__((always_inline)) {
+      constexpr int ST = decltype(stage_tag)::value;
+      // blocks n+1, n+2 (issued earlier) may stay in flight; block n must have landed everywhere
+      const int ahead = min(nblk - 1 - n, MNST - 2);
+      if (ahead >= 2) wait_wave_blocks<2>();
+      else if (ahead == 1) wait_wave_blocks<1>();
+      else wait_wave_blocks<0>();
+      __syncthreads();  // block n is in LDS, and every wave is done with block n-1's stage
+      if (n + MNST - 1 < nblk) issue(n + MNST - 1, std::integral_constant<int, (ST + MNST - 1) % MNST>{});
+      const bf16_t* lat = lds + ST * MSTAGE;
+      const bf16_t* rop = lat + LAT_STAGE;
+
+      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 16; ks += 2) {
+        s0 = mfma16k32(*(const bf16x8*)(lat + lat_s[ks]), qf[ks], s0);
+        s1 = mfma16k32(*(const bf16x8*)(lat + lat_s[ks + 1]), qf[ks + 1], s1);
+      }
+      s0 = mfma16k32(*(const bf16x8*)(rop + rope_s[0]), qf[16], s0);
+      s1 = mfma16k32(*(const bf16x8*)(rop + rope_s[1]), qf[17], s1);
+      // lane: keys 4G + v of the block for row i16 (every wave holds the whole score block)
+      const int j0 = ks0 + n * MKB + 4 * G;
+      float sv[4];
+      float mx = SOC_NEG_INF;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int j = j0 + v;
+        sv[v] = (j < ks1 && j <= pos) ? s0[v] + s1[v] : SOC_NEG_INF;
+        mx = fmaxf(mx, sv[v]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_cand = mx * c;
+      const bool upd = m_cand > m_run + 8.0f;
+      if (__builtin_amdgcn_ballot_w64(upd) != 0) {
+        asm volatile("");  // keeps this a branch: the rescale is rare
+        const float m_new = upd ? m_cand : m_run;
+        const float alpha = upd ? fast_exp2(m_run - m_new) : 1.f;
+        l_run *= alpha;
+#pragma unroll
+        for (int d = 0; d < 8; ++d)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) oacc[d][v] *= alpha;
+        m_run = m_new;
+      }
+      const float nm = (m_run == SOC_NEG_INF) ? 0.f : -m_run;
+      bf16x4 pb;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float p = fast_exp2(fmaf(sv[v], c, nm));
+        l_run += p;
+        pb[v] = (bf16_t)p;
+      }
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(lat + trb[w]));
+        oacc[w] = mfma16k16(__builtin_bit_cast(bf16x4, va), pb, oacc[w]);
+      }
+    };
+
+    for (int n = 0; n < nblk; n += MNST) {
+      step(n, std::integral_constant<int, 0>{});
+      if (n + 1 < nblk) step(n + 1, std::integral_constant<int, 1>{});
+      if (n + 2 < nblk) step(n + 2, std::integral_constant<int, 2>{});
+      if (n + 3 < nblk) step(n + 3, std::integral_constant<int, 3>{});
+    }
+
+    // the row's sum over the 4 lanes that share it
+    l_run += __shfl_xor(l_run, 16, 64);
+    l_run += __shfl_xor(l_run, 32, 64);
+    if (row_ok) {
+      const int64_t prow = ((int64_t)b * R + rho) * a.nsplit + s;
+      float* po = a.part_o + prow * MR + 128 * wave;  // this wave's dims 128 wave + 16 w + 4 G + v
+#pragma unroll
+      for (int w = 0; w < 8; ++w) *(f32x4*)(po + 16 * w + 4 * G) = oacc[w];
+      if (wave == 0 && G == 0) {
+        a.part_ml[2 * prow] = m_run;
+        a.part_ml[2 * prow + 1] = l_run;
+      }
+    }
+  }  // work loop
+}
+
+// Merge of one row's splits for 256 latent dims per workgroup (grid: rows x 2):
+// o_lat[d] = sum_s 2^(m_s - M) o_s[d] / sum_s 2^(m_s - M) l_s, M = max_s m_s (0 if no token).
+__global__ void __launch_bounds__(256) mla_merge_kernel(MlaArgs a) {
+  __shared__ float wgt[kMlaMaxSplits];
+  __shared__ float inv_l;
+  const int row = blockIdx.x >> 1, half = blockIdx.x & 1;  // row = b * R + rho
+  const int R = a.H * a.tq;
+  const int b = row / R, t = (row % R) % a.tq;
+  const int off = a.cache_off ? a.cache_off[b] : a.tk - a.tq;
+  const int nsb = (off + a.tq + a.split - 1) / a.split;
+  const int64_t p0 = (int64_t)row * a.nsplit;
+  (void)t;
+  if (threadIdx.x < 64) {  // wave 0: max over splits, then the weights and their sum
+    float M = SOC_NEG_INF;
+    for (int k = threadIdx.x; k < nsb; k += 64) M = fmaxf(M, a.part_ml[2 * (p0 + k)]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+    const float Ms = M == SOC_NEG_INF ? 0.f : M;
+    float L = 0.f;
+    for (int k = threadIdx.x; k < nsb; k += 64) {
+      const float m = a.part_ml[2 * (p0 + k)];
+      const float w = m == SOC_NEG_INF ? 0.f : fast_exp2(m - Ms);
+      wgt[k] = w;
+      L = fmaf(w, a.part_ml[2 * (p0 + k) + 1], L);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o, 64);
+    if (threadIdx.x == 0) inv_l = L > 0.f ? 1.f / L : 0.f;  // a row with no visible token outputs 0
+  }
+  __syncthreads();
+  const int d = half * 256 + threadIdx.x;
+  float acc = 0.f;
+  for (int k = 0; k < nsb; ++k) acc = fmaf(wgt[k], a.part_o[(p0 + k) * MR + d], acc);
+  a.o_lat[(int64_t)row * MR + d] = acc * inv_l;
+}
+
+// o[row, 32q + j] = sum_r o_lat[row, r] w_uv[h, r, 32q + j] for 16 rows (b, t) of head h
+// (grid: H x row groups x 4 quarters of the output width).
+__global__ void __launch_bounds__(256) mla_expand_kernel(MlaArgs a) {
+  __shared__ float ol[16][MR];
+  __shared__ __attribute__((aligned(16))) bf16_t ws[MR][32];  // w_uv[h][:, 32 q4 .. 32 q4 + 31]
+  const int q4 = blockIdx.x & 3;
+  const int hg = blockIdx.x >> 2;
+  const int h = hg % a.H, grp = hg / a.H;
+  const int nrow = a.B * a.tq;
+  const int R = a.H * a.tq;
+  for (int i = threadIdx.x; i < 16 * MR; i += 256) {
+    const int r = i / MR, d = i % MR, idx = grp * 16 + r;
+    float v = 0.f;
+    if (idx < nrow) {
+      const int b = idx / a.tq, t = idx % a.tq;
+      v = a.o_lat[((int64_t)b * R + h * a.tq + t) * MR + d];
+    }
+    ol[r][d] = v;
+  }
+  {  // the 512 x 32 weight slice in 16-byte pieces, all loads in flight at once
+    const bf16_t* wsrc = (const bf16_t*)a.w_uv + (int64_t)h * MR * MDV + 32 * q4;
+#pragma unroll
+    for (int k = 0; k < MR * 4 / 256; ++k) {
+      const int i = threadIdx.x + 256 * k, r = i >> 2, c = i & 3;
+      *(u32x4*)&ws[r][8 * c] = *(const u32x4*)(wsrc + (int64_t)r * MDV + 8 * c);
+    }
+  }
+  __syncthreads();
+  const int j = threadIdx.x & 31, rp = threadIdx.x >> 5;  // output dim 32 q4 + j, rows 2 rp, 2 rp + 1
+  const int dout = 32 * q4 + j;
+  float a0 = 0.f, a1 = 0.f;
+#pragma unroll 8
+  for (int r = 0; r < MR; ++r) {
+    const float w = (float)ws[r][j];
+    a0 = fmaf(ol[2 * rp][r], w, a0);
+    a1 = fmaf(ol[2 * rp + 1][r], w, a1);
+  }
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int idx = grp * 16 + 2 * rp + e;
+    if (idx < nrow) {
+      const int b = idx / a.tq, t = idx % a.tq;
+      ((bf16_t*)a.o)[b * a.o_sb + h * a.o_sh + t * a.o_st + dout] = (bf16_t)(e ? a1 : a0);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t s) {
+  const int64_t groups = ((int64_t)a.B * a.tq + 15) / 16;
+  const int64_t g1 = groups * a.H;
+  if (g1 == 0) return hipSuccess;
+  hipLaunchKernelGGL(mla_absorb_q_kernel, dim3((unsigned)(8 * g1)), dim3(64), 0, s, a);
+  const int64_t nrg = ((int64_t)a.H * a.tq + 15) / 16;
+  const int64_t items = (int64_t)a.B * nrg * a.nsplit;
+  const int64_t wgs = items < a.n_waves ? items : a.n_waves;
+  hipLaunchKernelGGL(mla_split_kernel, dim3((unsigned)wgs), dim3(256), 0, s, a);
+  const int64_t rows = (int64_t)a.B * a.H * a.tq;
+  hipLaunchKernelGGL(mla_merge_kernel, dim3((unsigned)(2 * rows)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(mla_expand_kernel, dim3((unsigned)(4 * g1)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace soc

@@ -213,3 +213,39 @@ def ring_step(B, Hq, Hkv, d, step, seed=0, dtype=torch.bfloat16):
     base = seed + 1000 + 10 * step
     return (normal((B, Hq, 1, d), base + SEED_Q, dtype), normal((B, Hkv, 1, d), base + SEED_K, dtype),
             normal((B, Hkv, 1, d), base + SEED_V, dtype))
+
+
+@dataclass
+class MlaCache:
+    """A latent KV cache (multi-head latent attention) with random projection weights.
+
+    c_kv [B, cap, 512], k_rope [B, cap, 64]: rows 0..L_b hold the cached tokens plus the
+    step's own token(s); q_nope [B, H, tq, 128], q_rope [B, H, tq, 64]; w_uk, w_uv
+    [H, 512, 128] drawn N(0, 1/128) and N(0, 1/512) so that folded queries and outputs stay
+    near unit scale; cache_off = L_b (the step's tokens sit at rows L_b .. L_b + tq - 1)."""
+
+    q_nope: torch.Tensor
+    q_rope: torch.Tensor
+    c_kv: torch.Tensor
+    k_rope: torch.Tensor
+    w_uk: torch.Tensor
+    w_uv: torch.Tensor
+    cache_off: torch.Tensor
+
+
+def mla_cache(B=64, H=16, lengths=None, lo=1024, hi=32768, tq=1, rank=512, rope=64, nope=128, dv=128, seed=0,
+              dtype=torch.bfloat16) -> MlaCache:
+    L = cache_lengths(B, lo, hi, seed) if lengths is None else torch.tensor(lengths, dtype=torch.int32)
+    cap = int(L.max()) + tq
+    c_kv = torch.zeros((B, cap, rank), dtype=dtype)
+    k_rope = torch.zeros((B, cap, rope), dtype=dtype)
+    gk = torch.Generator().manual_seed(seed + SEED_K)
+    for b in range(B):
+        n = int(L[b]) + tq
+        c_kv[b, :n] = torch.randn((n, rank), generator=gk).to(dtype)
+        k_rope[b, :n] = torch.randn((n, rope), generator=gk).to(dtype)
+    q_nope = normal((B, H, tq, nope), seed + SEED_Q, dtype)
+    q_rope = normal((B, H, tq, rope), seed + SEED_Q + 100, dtype)
+    w_uk = (normal((H, rank, nope), seed + SEED_V) / math.sqrt(nope)).to(dtype)
+    w_uv = (normal((H, rank, dv), seed + SEED_V + 100) / math.sqrt(rank)).to(dtype)
+    return MlaCache(q_nope, q_rope, c_kv, k_rope, w_uk, w_uv, L)
