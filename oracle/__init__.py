@@ -17,6 +17,8 @@ select  block selection by a mean-centroid score OR'd with a max-key-radius
 ring    a W-slot ring-buffer KV cache, an independent route to the window rule.
 mla     multi-head latent attention, plain (keys and values rebuilt per head) and
         absorbed (query moved into latent space, one shared latent KV head).
+dsa     token top-k sparse attention: an indexer's scores, the kept set per query
+        token, attention over it.
 brute   pure-Python scalar loops for tiny shapes (a second, independent
         implementation of both definitions).
 
