@@ -8,8 +8,9 @@ sliding-window prefill with sinks (T = 32768, W = 1024), KV-cache decode (batch 
 lengths uniform in [1024, 32768]; decode KV-read GB/s), a 512-token chunk appended at each
 sequence's cache offset, sliding-window decode over W = 1024-slot ring caches with the
 step's K/V appended (batch 64), multi-head latent attention decode in absorbed form
-(batch 64, 16 heads, 576 numbers per cached token), and block-sparse prefill (T = 65536,
-block 128) with its block selection.
+(batch 64, 16 heads, 576 numbers per cached token), token top-k sparse decode with its
+indexer (batch 64, top 2048), and block-sparse prefill (T = 65536, block 128) with its
+block selection.
 
 Algorithmic work: prefill flops = 4 * head_dim * sum over heads of the allowed (row, key)
 pairs (QK^T and PV, 2 flops per multiply-add; masked halves of tiles and the softmax are not
@@ -37,7 +38,7 @@ sys.path.insert(0, ROOT)
 
 import synth  # noqa: E402
 from sparse_offset_causal_amd import (attn_block_select, attn_decode, attn_decode_workspace_bytes,  # noqa: E402
-                                      attn_mla_decode, attn_mla_decode_workspace_bytes, attn_prefill,
+                                      attn_dsa_decode, attn_dsa_decode_workspace_bytes, attn_mla_decode, attn_mla_decode_workspace_bytes, attn_prefill,
                                       attn_ring_decode, attn_ring_decode_workspace_bytes)
 
 METRIC = "prefill TFLOP/s + decode KV-read GB/s, offset-causal GQA attention, 1 GPU"
@@ -194,6 +195,29 @@ def bench_mla_decode(steps, warmup, B=64, H=16):
     return r
 
 
+def bench_dsa_decode(steps, warmup, B=64, topk=2048):
+    """Token top-k sparse decode: batch 64, 32 query / 8 KV heads, cache lengths uniform in
+    [1024, 32768], 64 indexer heads of width 128, top 2048 tokens per query."""
+    x = synth.dsa_inputs(B=B)
+    q, k, v, qi, ki, wi = (t.cuda() for t in (x.q, x.k, x.v, x.qi, x.ki, x.wi))
+    off, sink = x.cache_off.cuda(), x.sink.cuda()
+    o = torch.empty_like(q)
+    ws = torch.empty(attn_dsa_decode_workspace_bytes(q, k, topk), dtype=torch.uint8, device="cuda")
+    fn = lambda: attn_dsa_decode(q, k, v, qi, ki, wi, topk, cache_off=off, sink=sink, workspace=ws, out=o)
+    r = Timer(fn, steps, warmup).run()
+    L = x.cache_off.numpy().astype(np.int64) + 1  # visible tokens per query
+    Hkv, d, Hq, Hi = 8, 128, 32, 64
+    idx_bytes = float((L * 128 * 2).sum())                                # every visible token's indexer key
+    kv_bytes = float((2 * Hkv * np.minimum(L, topk) * d * 2).sum())       # the kept K and V rows
+    other = float(2 * B * Hq * d * 2 + B * Hi * 128 * 2 + B * Hi * 4)    # q, o, qi, wi
+    nbytes = idx_bytes + kv_bytes + other
+    r.update(workload=f"dsa_decode_bf16_B{B}_cache1024-32768_{Hq}q{Hkv}kv_d{d}_idx{Hi}x128_top{topk}",
+             bytes_per_step=nbytes, value=nbytes / (r["ms_per_step"] * 1e-3) / 1e9,
+             kernel_GBps=nbytes / (r["launch_ms_mean"] * 1e-3) / 1e9, unit="GB/s")
+    del k, v
+    return r
+
+
 def bench_block_sparse(steps, warmup, T=65536, BS=128):
     w = synth.block_sparse_prefill(T=T, BS=BS)
     q, k, v, _, _ = to_dev(w)
@@ -273,7 +297,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", default="all",
-                    help="all | causal_prefill | window_sink | decode | ring_decode | mla_decode | block_sparse | copy (HBM counter calibration)")
+                    help="all | causal_prefill | window_sink | decode | ring_decode | mla_decode | dsa_decode | block_sparse | "
+                         "copy (HBM counter calibration)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="JSON file of HBM bytes per launch measured with rocprofv3 counters")
@@ -327,6 +352,11 @@ def main():
         also["mla_decode"] = r
         log(f"mla decode: {r['value']:.0f} GB/s ({r['ms_per_step']:.3f} ms)")
         torch.cuda.empty_cache()
+    if args.only in ("all", "dsa_decode"):
+        r = bench_dsa_decode(args.steps, args.warmup)
+        also["dsa_decode"] = r
+        log(f"dsa decode: {r['value']:.0f} GB/s ({r['ms_per_step']:.3f} ms)")
+        torch.cuda.empty_cache()
     if args.only in ("all", "block_sparse"):
         rs, rp = bench_block_sparse(args.steps, args.warmup)
         also["block_select"], also["block_sparse_prefill"] = rs, rp
@@ -335,7 +365,7 @@ def main():
         torch.cuda.empty_cache()
 
     if head is None:  # a single non-headline workload was requested: its main kernel heads the line
-        for key in ("window_sink_prefill", "decode", "ring_decode", "mla_decode", "block_sparse_prefill"):
+        for key in ("window_sink_prefill", "decode", "ring_decode", "mla_decode", "dsa_decode", "block_sparse_prefill"):
             if key in also:
                 head = also[key]
                 break

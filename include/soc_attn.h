@@ -210,6 +210,39 @@ int attn_mla_decode(const attn_mla_shape_t* shape, const void* q_nope, attn_stri
                     size_t workspace_bytes, int32_t split_tokens, hipStream_t stream);
 
 /*
+ * attn_dsa_decode_workspace_bytes -- device workspace for attn_dsa_decode (split_tokens
+ * <= 0 selects the default).  Returns 0 for an invalid shape.
+ */
+size_t attn_dsa_decode_workspace_bytes(const attn_shape_t* shape, int32_t topk, int32_t split_tokens);
+
+/*
+ * attn_dsa_decode -- token top-k sparse attention for a few query tokens per sequence
+ * (sotaaz.com/post/attention-in-code, section 5): an indexer scores every token a query
+ * token may see,
+ *     score(t, s) = sum over indexer heads j of wi[j, t] * relu(qi[j, t] . ki[s]),
+ * and every head of that query token attends only over its top-k visible tokens (all of
+ * them if fewer than k are visible; equal scores go to the lower token index).  The cache
+ * stays whole; only the kept rows of K and V are read.
+ *
+ *  q, k, v, o, cache_off, sink, scale: as attn_decode (bf16, head_dim 128; k/v hold tk rows
+ *             per sequence; query token t of sequence b sits at position off_b + t).
+ *  qi         [batch, index_heads, tq, 128] bf16;  ki [batch, tk, 128] bf16 (strides .b, .t;
+ *             .h ignored);  wi device float32 [batch, index_heads, tq], contiguous.
+ *  index_heads a multiple of 16, at most 64;  topk >= 1.
+ *  kept_list  device int32 [batch, tq, topk] or NULL: the kept token indices of each query
+ *             token in ascending order (entries past kept_count unspecified).
+ *  kept_count device int32 [batch, tq] or NULL.
+ *  workspace  at least attn_dsa_decode_workspace_bytes(shape, topk, split_tokens) bytes.
+ *  split_tokens: kept-list entries per split, at most 1024.  bf16 needs n_heads / n_kv <= 32.
+ */
+int attn_dsa_decode(const attn_shape_t* shape, const void* q, attn_strides_t q_strides, const void* k, const void* v,
+                    attn_strides_t kv_strides, void* o, attn_strides_t o_strides, const int32_t* cache_off,
+                    const float* sink, float scale, const void* qi, attn_strides_t qi_strides, const void* ki,
+                    attn_strides_t ki_strides, const float* wi, int32_t index_heads, int32_t topk,
+                    int32_t* kept_list, int32_t* kept_count, void* workspace, size_t workspace_bytes,
+                    int32_t split_tokens, hipStream_t stream);
+
+/*
  * attn_block_select_workspace_bytes -- device workspace for attn_block_select.
  */
 size_t attn_block_select_workspace_bytes(const attn_shape_t* shape, int32_t block_size);

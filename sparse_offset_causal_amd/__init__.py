@@ -7,6 +7,7 @@ The computation lives in hand-written HIP kernels behind the C ABI of
     attn_decode(q, k, v, cache_off=None, window=0, sink=None, scale=None, split_tokens=0)
     attn_ring_decode(q, k_new, v_new, k_ring, v_ring, n_seen, sink=None, scale=None)
     attn_mla_decode(q_nope, q_rope, c_kv, k_rope, w_uk, w_uv, cache_off=None)
+    attn_dsa_decode(q, k, v, qi, ki, wi, topk, cache_off=None, sink=None)
     attn_block_select(q, k, block_size=128, keep_mean=0.05, keep_radius=0.05, ...)
     attn_block_list_from_mask(mask)
 
@@ -20,6 +21,8 @@ from .api import (  # noqa: F401
     attn_block_select_workspace_bytes,
     attn_decode,
     attn_decode_workspace_bytes,
+    attn_dsa_decode,
+    attn_dsa_decode_workspace_bytes,
     attn_mla_decode,
     attn_mla_decode_workspace_bytes,
     attn_prefill,

@@ -18,6 +18,8 @@ EXPORTS = (
     "attn_ring_decode",
     "attn_mla_decode_workspace_bytes",
     "attn_mla_decode",
+    "attn_dsa_decode_workspace_bytes",
+    "attn_dsa_decode",
     "attn_block_select_workspace_bytes",
     "attn_block_select",
     "attn_block_list_from_mask",
@@ -71,6 +73,12 @@ def load() -> ctypes.CDLL:
     lib.attn_mla_decode.argtypes = [POINTER(AttnMlaShape), P, AttnStrides, P, AttnStrides, P, AttnStrides, P,
                                     AttnStrides, P, P, P, AttnStrides, P, c_float, P, c_size_t, c_int32, P]
     lib.attn_mla_decode.restype = c_int
+    lib.attn_dsa_decode_workspace_bytes.argtypes = [POINTER(AttnShape), c_int32, c_int32]
+    lib.attn_dsa_decode_workspace_bytes.restype = c_size_t
+    lib.attn_dsa_decode.argtypes = [POINTER(AttnShape), P, AttnStrides, P, P, AttnStrides, P, AttnStrides, P, P,
+                                    c_float, P, AttnStrides, P, AttnStrides, P, c_int32, c_int32, P, P, P, c_size_t,
+                                    c_int32, P]
+    lib.attn_dsa_decode.restype = c_int
     lib.attn_block_select_workspace_bytes.argtypes = [POINTER(AttnShape), c_int32]
     lib.attn_block_select_workspace_bytes.restype = c_size_t
     lib.attn_block_select.argtypes = [POINTER(AttnShape), P, AttnStrides, P, AttnStrides, P, c_int32, c_int32,

@@ -210,6 +210,40 @@ def attn_mla_decode(q_nope, q_rope, c_kv, k_rope, w_uk, w_uv, cache_off=None, sc
     return out
 
 
+def attn_dsa_decode_workspace_bytes(q, k, topk, split_tokens=0) -> int:
+    return int(_lib.load().attn_dsa_decode_workspace_bytes(_shape(q, k), int(topk), int(split_tokens)))
+
+
+def attn_dsa_decode(q, k, v, qi, ki, wi, topk, cache_off=None, sink=None, scale=None, split_tokens=0,
+                    want_kept=False, workspace=None, out=None):
+    """Token top-k sparse attention decode (see attn_dsa_decode in include/soc_attn.h): q [B,Hq,Tq,128],
+    k, v [B,Hkv,Tk,128], qi [B,Hi,Tq,128], ki [B,Tk,128] (token axis strided), wi float32 [B,Hi,Tq].
+    Returns o, or (o, kept_list [B,Tq,topk], kept_count [B,Tq]) with want_kept."""
+    _common(q, k, v, cache_off, sink)
+    _check4("qi", qi)
+    if ki.dim() != 3 or not ki.is_cuda or ki.stride(2) != 1 or ki.dtype != q.dtype:
+        raise ValueError("ki must be a 3-D GPU tensor [batch, tokens, 128] in q's dtype with a contiguous last axis")
+    if wi.dtype != torch.float32 or not wi.is_cuda or not wi.is_contiguous() or wi.shape != (q.shape[0], qi.shape[1], q.shape[2]):
+        raise ValueError("wi must be a contiguous float32 GPU tensor [batch, index_heads, tq]")
+    o = _out(q, out)
+    lib = _lib.load()
+    shape = _shape(q, k)
+    need = int(lib.attn_dsa_decode_workspace_bytes(shape, int(topk), int(split_tokens)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    kl = kc = None
+    if want_kept:
+        kl = torch.empty((q.shape[0], q.shape[2], int(topk)), dtype=torch.int32, device=q.device)
+        kc = torch.empty((q.shape[0], q.shape[2]), dtype=torch.int32, device=q.device)
+    rc = lib.attn_dsa_decode(shape, q.data_ptr(), _strides(q), k.data_ptr(), v.data_ptr(), _strides(k), o.data_ptr(),
+                             _strides(o), _ptr(cache_off), _ptr(sink), float(scale or 0.0), qi.data_ptr(),
+                             _strides(qi), ki.data_ptr(), AttnStrides(ki.stride(0), 0, ki.stride(1)), wi.data_ptr(),
+                             int(qi.shape[1]), int(topk), _ptr(kl), _ptr(kc), workspace.data_ptr(),
+                             workspace.numel() * workspace.element_size(), int(split_tokens), _stream())
+    _check(rc)
+    return (o, kl, kc) if want_kept else o
+
+
 def attn_block_select_workspace_bytes(q, k, block_size=128) -> int:
     return int(_lib.load().attn_block_select_workspace_bytes(_shape(q, k), int(block_size)))
 

@@ -14,7 +14,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsoc_attn.so")
 
-SOURCES = ["abi.cpp", "prefill_bf16.hip", "decode_bf16.hip", "attn_f32.hip", "blocksel.hip", "ring.hip", "mla_bf16.hip"]
+SOURCES = ["abi.cpp", "prefill_bf16.hip", "decode_bf16.hip", "attn_f32.hip", "blocksel.hip", "ring.hip", "mla_bf16.hip", "dsa_bf16.hip"]
 
 # Packed fp32 VALU ops are turned off for device code (the host pass ignores the feature).
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-Wall", "-Wno-unused-function",

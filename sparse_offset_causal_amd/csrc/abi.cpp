@@ -229,6 +229,30 @@ MlaLayout mla_layout(const attn_mla_shape_t* s, int32_t split_tokens) {
   return L;
 }
 
+struct DsaLayout {
+  size_t part, scores, list, count, total;
+  int split, nsplit;
+};
+
+DsaLayout dsa_layout(const attn_shape_t* s, int topk, int32_t split_tokens) {
+  DsaLayout L{};
+  L.split = split_tokens > 0 ? split_tokens : 256;
+  L.nsplit = topk > 0 ? (topk + L.split - 1) / L.split : 1;
+  const size_t rows = (size_t)s->batch * s->n_heads * s->tq;
+  const size_t qrows = (size_t)s->batch * s->tq;
+  size_t off = 0;
+  L.part = off;
+  off = round_up(off + rows * L.nsplit * (s->head_dim + 2) * sizeof(float), 256);
+  L.scores = off;
+  off = round_up(off + qrows * (size_t)s->tk * sizeof(float), 256);
+  L.list = off;
+  off = round_up(off + qrows * (size_t)(topk > 0 ? topk : 1) * sizeof(int32_t), 256);
+  L.count = off;
+  off = round_up(off + qrows * sizeof(int32_t), 256);
+  L.total = off;
+  return L;
+}
+
 }  // namespace
 
 extern "C" {
@@ -463,6 +487,69 @@ int attn_mla_decode(const attn_mla_shape_t* shape, const void* q_nope, attn_stri
   a.split = L.split;
   a.n_waves = 2 * device_cus();  // the split kernel's LDS use allows two waves per CU
   return finish(soc::launch_mla_decode(a, stream), stream, "attn_mla_decode launch");
+}
+
+size_t attn_dsa_decode_workspace_bytes(const attn_shape_t* shape, int32_t topk, int32_t split_tokens) {
+  if (check_shape(shape) != ATTN_OK || topk < 1) return 0;
+  return dsa_layout(shape, topk, split_tokens).total;
+}
+
+int attn_dsa_decode(const attn_shape_t* shape, const void* q, attn_strides_t q_strides, const void* k, const void* v,
+                    attn_strides_t kv_strides, void* o, attn_strides_t o_strides, const int32_t* cache_off,
+                    const float* sink, float scale, const void* qi, attn_strides_t qi_strides, const void* ki,
+                    attn_strides_t ki_strides, const float* wi, int32_t index_heads, int32_t topk,
+                    int32_t* kept_list, int32_t* kept_count, void* workspace, size_t workspace_bytes,
+                    int32_t split_tokens, hipStream_t stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if (shape->dtype != ATTN_BF16 || shape->head_dim != 128)
+    return fail(ATTN_E_UNSUPPORTED, "sparse top-k decode is built for bf16 with head_dim 128");
+  if (topk < 1) return fail(ATTN_E_INVAL, "topk must be >= 1");
+  if (index_heads < 16 || index_heads > soc::kDsaMaxIndexHeads || index_heads % 16 != 0)
+    return fail(ATTN_E_UNSUPPORTED, "index_heads must be 16, 32, 48 or 64");
+  if (shape->tq == 0 || shape->batch == 0) {
+    g_err.clear();
+    return ATTN_OK;
+  }
+  if ((rc = check_tensors(shape, q, q_strides, k, v, kv_strides, o, o_strides))) return rc;
+  if (!qi || !ki || !wi) return fail(ATTN_E_INVAL, "qi, ki and wi must be non-NULL device pointers");
+  if (!aligned16(qi) || !aligned16(ki)) return fail(ATTN_E_INVAL, "qi and ki must be 16-byte aligned");
+  const attn_strides_t ki_bt{ki_strides.b, 0, ki_strides.t};
+  if (!strides_ok(qi_strides, 2) || !strides_ok(ki_bt, 2))
+    return fail(ATTN_E_INVAL, "strides must be non-negative multiples of 16 bytes (in elements)");
+  if (ki_strides.t < soc::kDsaIndexDim) return fail(ATTN_E_INVAL, "ki token stride must be at least 128");
+  if ((shape->n_heads / shape->n_kv) > 32)
+    return fail(ATTN_E_UNSUPPORTED, "bf16 decode serves at most 32 query rows per KV head (n_heads/n_kv <= 32)");
+  if ((int64_t)shape->tk * kv_strides.t * 2 > (int64_t)0x7fffffff || (int64_t)shape->tk * ki_strides.t * 2 > (int64_t)0x7fffffff)
+    return fail(ATTN_E_UNSUPPORTED, "one (sequence, KV head) cache slice spans more than 2 GiB");
+  const DsaLayout L = dsa_layout(shape, topk, split_tokens);
+  if (L.split > 1024) return fail(ATTN_E_INVAL, "split_tokens must be at most 1024");
+  if (!workspace) return fail(ATTN_E_WORKSPACE, "workspace is NULL");
+  if (!aligned16(workspace)) return fail(ATTN_E_WORKSPACE, "workspace must be 16-byte aligned");
+  if (workspace_bytes < L.total)
+    return fail(ATTN_E_WORKSPACE, "workspace too small: need " + std::to_string(L.total) + " bytes");
+  if ((int64_t)shape->batch * shape->tq * shape->n_kv * L.nsplit >= (int64_t)1 << 31 ||
+      (int64_t)shape->batch * shape->tq * ((shape->tk + 255) / 256) >= (int64_t)1 << 31)
+    return fail(ATTN_E_INVAL, "problem too large for one grid");
+  if ((rc = check_offsets_debug(shape, cache_off, stream))) return rc;
+
+  soc::DsaArgs A{};
+  A.at = make_args(shape, q, q_strides, k, v, kv_strides, o, o_strides, cache_off, 0, sink, scale);
+  char* ws = static_cast<char*>(workspace);
+  A.at.part = reinterpret_cast<float*>(ws + L.part);
+  A.at.nsplit = L.nsplit;
+  A.at.split = L.split;
+  A.qi = qi;
+  A.qi_sb = qi_strides.b; A.qi_sh = qi_strides.h; A.qi_st = qi_strides.t;
+  A.ki = ki;
+  A.ki_sb = ki_strides.b; A.ki_st = ki_strides.t;
+  A.wi = wi;
+  A.Hi = index_heads;
+  A.topk = topk;
+  A.scores = reinterpret_cast<float*>(ws + L.scores);
+  A.list = kept_list ? kept_list : reinterpret_cast<int32_t*>(ws + L.list);
+  A.count = kept_count ? kept_count : reinterpret_cast<int32_t*>(ws + L.count);
+  return finish(soc::launch_dsa_decode(A, stream), stream, "attn_dsa_decode launch");
 }
 
 size_t attn_block_select_workspace_bytes(const attn_shape_t* shape, int32_t block_size) {

@@ -1,0 +1,411 @@
+// Token top-k sparse attention decode for gfx950 (bf16 in, fp32 accumulate, head_dim 128).
+//
+// A small scorer (the indexer) rates every token a query token may see, and attention runs
+// only over the k best-rated ones; the cache stays whole (sotaaz.com/post/attention-in-code,
+// section 5).  Indexer score of cached token s for query token t:
+//   sum over indexer heads j of w[j, t] * relu(qi[j, t] . ki[s]).
+// The kept set of a query token is its top k visible tokens (all of them if fewer are
+// visible); equal scores go to the lower token index.  Every head of the query token attends
+// over the same kept set.
+//
+//   dsa_indexer_kernel  one wave per (sequence, query token, 256 tokens): scores^T = Ki Qi^T
+//                       with v_mfma_f32_16x16x32_bf16 (16 tokens x 16 indexer heads per MFMA),
+//                       ReLU and the head weights in fp32, the sum over heads in a fixed order
+//   dsa_topk_kernel     one 1024-thread workgroup per (sequence, query token): 4-pass radix
+//                       select of the k-th largest score on order-preserving 32-bit keys, then
+//                       an index-ordered compaction (ties at the threshold: lowest indices)
+//                       into an ascending list
+//   dsa_split_kernel    split-KV decode over the kept list: one wave per (sequence, KV head,
+//                       query token, split of the list); K rows are gathered by index straight
+//                       into registers and V rows by index into LDS (buffer loads with the LDS
+//                       bit, per-lane offsets from the list), then the same MFMA / online
+//                       softmax scheme as the dense decode; partials merge in decode_merge.
+
+#include <type_traits>
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace soc {
+namespace {
+
+constexpr int D = 128;
+constexpr int DI = kDsaIndexDim;
+constexpr int KB = 32;
+constexpr int NST = 3;
+constexpr int VSTAGE = KB * D;
+constexpr int MAX_SPLIT = 1024;  // kept-list entries per split (staged in LDS)
+constexpr float RESCALE_SLACK = 8.0f;
+
+typedef short s16x4 __attribute__((__vector_size__(8)));
+typedef short s16x8 __attribute__((__vector_size__(16)));
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
+
+__device__ __forceinline__ f32x4 mfma16k32(bf16x8 a, bf16x8 b, f32x4 c) {
+  // lane l: A[l%16][8(l/16)+e], B[8(l/16)+e][l%16], D[4(l/16)+v][l%16]
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ uint32_t f32_order_key(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  return (u >> 31) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ int seq_off(const AttnArgs& a, int b) { return a.cache_off ? a.cache_off[b] : a.tk - a.tq; }
+
+// ---------------------------------------------------------------------------------------
+__global__ void __launch_bounds__(64) dsa_indexer_kernel(DsaArgs A) {
+  const AttnArgs& a = A.at;
+  const int lane = threadIdx.x, G = lane >> 4, i16 = lane & 15;
+  const int nch = (a.tk + 255) / 256;
+  int bid = blockIdx.x;
+  const int ch = bid % nch;
+  bid /= nch;
+  const int t = bid % a.tq, b = bid / a.tq;
+  const int n_vis = min(a.tk, seq_off(a, b) + t + 1);
+  const int s0 = ch * 256;
+  if (s0 >= n_vis) return;
+  const int nhb = A.Hi / 16;
+  bf16x8 qb[4][4];
+  float w[4];
+  const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb) {
+    const int head = 16 * hb + i16;
+    const bool ok = hb < nhb;
+    const bf16_t* qp = (const bf16_t*)A.qi + b * A.qi_sb + head * A.qi_sh + t * A.qi_st;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qb[hb][ks] = ok ? *(const bf16x8*)(qp + 32 * ks + 8 * G) : as_bf16x8(z);
+    w[hb] = ok ? A.wi[((int64_t)b * A.Hi + head) * a.tq + t] : 0.f;
+  }
+  const uint32_t row_bytes = (uint32_t)A.ki_st * 2u;
+  const bf16_t* kp = (const bf16_t*)A.ki + b * A.ki_sb;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kp, (short)0, (int)(n_vis * row_bytes), 0x00020000);
+  float* out = A.scores + ((int64_t)b * a.tq + t) * a.tk;
+  for (int blk = 0; blk < 16; ++blk) {
+    const int tok0 = s0 + 16 * blk;
+    if (tok0 >= n_vis) break;
+    bf16x8 af[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      af[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                              krs, (uint32_t)(tok0 + i16) * row_bytes + (uint32_t)(64 * ks + 16 * G), 0, 0));
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) {
+      if (hb >= nhb) break;  // uniform
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) acc = mfma16k32(af[ks], qb[hb][ks], acc);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) part[v] = fmaf(w[hb], fmaxf(acc[v], 0.f), part[v]);
+    }
+    // lane (G, i16): tokens 4G + v, indexer head i16 of each block; sum over the 16 heads
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) part[v] += __shfl_xor(part[v], m, 64);
+    if (i16 == 0) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int tok = tok0 + 4 * G + v;
+        if (tok < n_vis) out[tok] = part[v];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Wave-wide search in descending order over 64 lanes x 4 bins (lane l: bins 4l..4l+3).
+__device__ void locate_digit(const unsigned* hist, unsigned rank, unsigned* digit, unsigned* rank_in) {
+  const int lane = threadIdx.x & 63;
+  const unsigned c = hist[4 * lane] + hist[4 * lane + 1] + hist[4 * lane + 2] + hist[4 * lane + 3];
+  unsigned s = c;  // inclusive suffix sum over lanes >= this one
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const unsigned y = __shfl_down(s, o, 64);
+    if (lane + o < 64) s += y;
+  }
+  const unsigned ab = s - c;
+  const unsigned long long own = __ballot(ab <= rank && rank < s);
+  const int L = own ? __ffsll(own) - 1 : 0;
+  unsigned r = rank - __shfl(ab, L, 64);
+  int e = 3;
+  for (; e > 0; --e) {
+    const unsigned h = hist[4 * L + e];
+    if (r < h) break;
+    r -= h;
+  }
+  *digit = 4 * L + e;
+  *rank_in = r;
+}
+
+// Block-wide exclusive prefix count of `flag` (1024 threads) plus the block total.
+__device__ __forceinline__ unsigned block_prefix(bool flag, unsigned* wsum, unsigned* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const unsigned long long bal = __ballot(flag);
+  const unsigned before = __popcll(bal & ((1ull << lane) - 1ull));
+  if (lane == 0) wsum[wave] = __popcll(bal);
+  __syncthreads();
+  unsigned wbase = 0, tot = 0;
+  for (int w = 0; w < 16; ++w) {
+    const unsigned c = wsum[w];
+    if (w < wave) wbase += c;
+    tot += c;
+  }
+  __syncthreads();
+  *total = tot;
+  return wbase + before;
+}
+
+constexpr int TOPK_LDS = 32768;  // scores of up to this many visible tokens are staged in LDS
+
+__global__ void __launch_bounds__(1024) dsa_topk_kernel(DsaArgs A) {
+  const AttnArgs& a = A.at;
+  __shared__ unsigned hist[256];
+  __shared__ unsigned su[2];
+  __shared__ unsigned wsum[16];
+  __shared__ uint32_t keys[TOPK_LDS];
+  const int t = blockIdx.x % a.tq, b = blockIdx.x / a.tq;
+  const int n_vis = min(a.tk, seq_off(a, b) + t + 1);
+  const int K = A.topk;
+  int32_t* lst = A.list + ((int64_t)b * a.tq + t) * K;
+  if (n_vis <= K) {  // every visible token is kept
+    for (int j = threadIdx.x; j < n_vis; j += 1024) lst[j] = j;
+    if (threadIdx.x == 0) A.count[b * a.tq + t] = n_vis;
+    return;
+  }
+  const float* sc = A.scores + ((int64_t)b * a.tq + t) * a.tk;
+  const bool staged = n_vis <= TOPK_LDS;
+  if (staged)
+    for (int i = threadIdx.x; i < n_vis; i += 1024) keys[i] = f32_order_key(sc[i]);
+  auto key_at = [&](int i) __attribute__((always_inline)) { return staged ? keys[i] : f32_order_key(sc[i]); };
+  // radix select of the key at descending rank K - 1
+  unsigned prefix = 0, pmask = 0, rank = (unsigned)(K - 1);
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    if (threadIdx.x < 256) hist[threadIdx.x] = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < n_vis; i += 1024) {
+      const uint32_t key = key_at(i);
+      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      unsigned dg, r;
+      locate_digit(hist, rank, &dg, &r);
+      if (threadIdx.x == 0) {
+        su[0] = prefix | (dg << shift);
+        su[1] = r;
+      }
+    }
+    __syncthreads();
+    prefix = su[0];
+    rank = su[1];
+    pmask |= 255u << shift;
+    __syncthreads();
+  }
+  // keys above the threshold, then the first rank + 1 keys equal to it in token order
+  const uint32_t tau = prefix;
+  const unsigned need_eq = rank + 1;
+  unsigned base = 0, eq_base = 0;
+  for (int c0 = 0; c0 < n_vis; c0 += 1024) {
+    const int i = c0 + threadIdx.x;
+    const uint32_t key = i < n_vis ? key_at(i) : 0u;
+    const bool gt = i < n_vis && key > tau;
+    const bool eq = i < n_vis && key == tau;
+    unsigned eq_tot, keep_tot;
+    const unsigned eq_rank = eq_base + block_prefix(eq, wsum, &eq_tot);
+    const bool keep = gt || (eq && eq_rank < need_eq);
+    const unsigned pos = base + block_prefix(keep, wsum, &keep_tot);
+    if (keep) lst[pos] = i;
+    base += keep_tot;
+    eq_base += eq_tot;
+  }
+  if (threadIdx.x == 0) A.count[b * a.tq + t] = K;
+}
+
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ int v_off(int row, int chunk) { return row * D + ((chunk ^ ((row & 3) << 2)) << 3); }
+
+__device__ __forceinline__ void wait_blocks(int blocks_after) {
+  static_assert(NST - 1 <= 3, "vmcnt holds at most 63 outstanding loads: 3 blocks of 16");
+  if (blocks_after >= 2)
+    asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
+  else if (blocks_after == 1)
+    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) dsa_split_kernel(DsaArgs A) {
+  const AttnArgs& a = A.at;
+  __shared__ __attribute__((aligned(1024))) bf16_t vlds[NST * VSTAGE];
+  __shared__ int32_t ent[MAX_SPLIT];
+
+  const int lane = threadIdx.x;
+  const int l32 = lane & 31, hh = lane >> 5;
+  int bid = blockIdx.x;
+  const int s = __builtin_amdgcn_readfirstlane(bid % a.nsplit);
+  bid /= a.nsplit;
+  const int t = __builtin_amdgcn_readfirstlane(bid % a.tq);
+  bid /= a.tq;
+  const int kvh = __builtin_amdgcn_readfirstlane(bid % a.Hkv);
+  const int b = __builtin_amdgcn_readfirstlane(bid / a.Hkv);
+  const int cnt = __builtin_amdgcn_readfirstlane(A.count[b * a.tq + t]);
+  const int ks0 = s * a.split, ks1 = min(ks0 + a.split, cnt);
+  const int nblk = ks0 < ks1 ? (ks1 - ks0 + KB - 1) / KB : 0;
+  const int32_t* lst = A.list + ((int64_t)b * a.tq + t) * A.topk;
+  for (int i = lane; i < nblk * KB; i += 64) ent[i] = ks0 + i < ks1 ? lst[ks0 + i] : 0;
+
+  // query rows: the g heads of KV head kvh at query token t (lane l32 = head in group)
+  const bool row_ok = l32 < a.g;
+  const int h = kvh * a.g + (row_ok ? l32 : 0);
+  const bf16_t* qp = (const bf16_t*)a.q + b * a.q_sb + h * a.q_sh + (int64_t)t * a.q_st;
+  bf16x8 qf[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    u32x4 z = {0u, 0u, 0u, 0u};
+    qf[ks] = row_ok ? *(const bf16x8*)(qp + 16 * ks + 8 * hh) : as_bf16x8(z);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the list and q are in; only block loads are counted below
+  __syncthreads();
+
+  const uint32_t row_bytes = (uint32_t)a.kv_st * 2u;
+  const bf16_t* kp = (const bf16_t*)a.k + b * a.kv_sb + kvh * a.kv_sh;
+  const bf16_t* vp = (const bf16_t*)a.v + b * a.kv_sb + kvh * a.kv_sh;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kp, (short)0, (int)(a.tk * row_bytes), 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vp, (short)0, (int)(a.tk * row_bytes), 0x00020000);
+  const int vr = lane >> 4;
+  const uint32_t v_sw = (uint32_t)(((lane & 15) ^ ((vr & 3) << 2)) << 4);
+
+  bf16x8 kreg[NST][8];
+  auto issue = [&](int n, auto stage_tag) __attribute__((always_inline)) {
+    constexpr int ST = decltype(stage_tag)::value;
+    const uint32_t krow = (uint32_t)ent[n * KB + l32] * row_bytes;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      kreg[ST][ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(krs, krow + hh * 16 + ks * 32, 0, 0));
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void_ptr)(vlds + ST * VSTAGE + i * 512), 16,
+                                               (uint32_t)ent[n * KB + 4 * i + vr] * row_bytes + v_sw, 0, 0, 0);
+  };
+  if (nblk > 0) issue(0, std::integral_constant<int, 0>{});
+  if (nblk > 1) issue(1, std::integral_constant<int, 1>{});
+
+  f32x16 oacc[4];
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) oacc[tb][v] = 0.f;
+  float m_run = SOC_NEG_INF, l_run = 0.f;
+  const float c = a.scale_log2;
+  int voff[4];
+  {
+    const int trj = lane & 15;
+    const int tr_row = 4 * hh + (trj >> 2);
+    const int tr_col = ((lane >> 4) & 1) * 16 + 4 * (trj & 3);
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      const int col = tb * 32 + tr_col;
+      voff[tb] = v_off(tr_row, col >> 3) + (col & 7);
+    }
+  }
+
+  auto step = [&](int n, auto stage_tag) __attribute__((always_inline)) {
+    constexpr int ST = decltype(stage_tag)::value;
+    if (n + NST - 1 < nblk) issue(n + NST - 1, std::integral_constant<int, (ST + NST - 1) % NST>{});
+    wait_blocks(min(NST - 1, nblk - 1 - n));
+    const bf16_t* vt = vlds + ST * VSTAGE;
+    const int js = ks0 + n * KB;  // list position of the block's first entry
+
+    f32x16 sacc;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) sacc[v] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) sacc = mfma32x32x16(kreg[ST][ks], qf[ks], sacc);
+    float mx = SOC_NEG_INF;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int j = js + 8 * (v >> 2) + 4 * hh + (v & 3);
+      sacc[v] = j < ks1 ? sacc[v] : SOC_NEG_INF;  // the list holds visible tokens only
+      mx = fmaxf(mx, sacc[v]);
+    }
+    mx = pair_max(mx);
+    const float m_cand = mx * c;
+    const bool upd = m_cand > m_run + RESCALE_SLACK;
+    if (__builtin_amdgcn_ballot_w64(upd) != 0) {
+      asm volatile("");  // keeps this a branch: the rescale is rare
+      const float m_new = upd ? m_cand : m_run;
+      const float alpha = upd ? fast_exp2(m_run - m_new) : 1.f;
+      l_run *= alpha;
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) oacc[tb][v] *= alpha;
+      m_run = m_new;
+    }
+    const float nm = (m_run == SOC_NEG_INF) ? 0.f : -m_run;
+    bf16x8 pb[2];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const float p = fast_exp2(fmaf(sacc[v], c, nm));
+      l_run += p;
+      pb[v >> 3][v & 7] = (bf16_t)p;
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vt + 16 * kk * D + voff[tb]));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_ptr)(vt + (16 * kk + 8) * D + voff[tb]));
+        const s16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        oacc[tb] = mfma32x32x16(__builtin_bit_cast(bf16x8, va), pb[kk], oacc[tb]);
+      }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this stage's LDS reads finish before its refill
+  };
+
+  for (int n = 0; n < nblk; n += NST) {
+    step(n, std::integral_constant<int, 0>{});
+    if (n + 1 < nblk) step(n + 1, std::integral_constant<int, 1>{});
+    if (n + 2 < nblk) step(n + 2, std::integral_constant<int, 2>{});
+  }
+
+  // every split writes its partial, an empty one (max -inf, sum 0, O 0) included
+  const float L = pair_sum(l_run);
+  if (row_ok) {
+    const int64_t rowid = ((int64_t)b * a.Hq + h) * a.tq + t;
+    float* po = a.part + (rowid * a.nsplit + s) * D;
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        f32x4 out;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[e] = oacc[tb][4 * g4 + e];
+        *(f32x4*)(po + tb * 32 + 8 * g4 + 4 * hh) = out;
+      }
+    if (hh == 0) {
+      float* pml = a.part + decode_o_floats(a) + (rowid * a.nsplit + s) * 2;
+      pml[0] = m_run;
+      pml[1] = L;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_dsa_decode(const DsaArgs& A, hipStream_t s) {
+  const AttnArgs& a = A.at;
+  const int64_t rows = (int64_t)a.B * a.tq;
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(dsa_indexer_kernel, dim3((unsigned)(rows * ((a.tk + 255) / 256))), dim3(64), 0, s, A);
+  hipLaunchKernelGGL(dsa_topk_kernel, dim3((unsigned)rows), dim3(1024), 0, s, A);
+  hipLaunchKernelGGL(dsa_split_kernel, dim3((unsigned)(rows * a.Hkv * a.nsplit)), dim3(64), 0, s, A);
+  // every split has a partial: the merge reads all nsplit of them (no offsets, tk = nsplit * split)
+  AttnArgs m = a;
+  m.cache_off = nullptr;
+  m.tk = a.nsplit * a.split;
+  return launch_decode_merge(m, true, s);
+}
+
+}  // namespace soc

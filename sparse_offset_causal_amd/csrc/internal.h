@@ -112,6 +112,22 @@ struct MlaArgs {
   int32_t nsplit, split;
   int32_t n_waves;  // persistent split waves
 };
+// Token top-k sparse attention decode (bf16, head_dim 128, indexer width 128).
+constexpr int kDsaIndexDim = 128, kDsaMaxIndexHeads = 64;
+struct DsaArgs {
+  AttnArgs at;          // q, k, v, o, strides, shape, cache_off, sink, scale, part/nsplit/split
+  const void* qi;       // [B, Hi, tq, 128]
+  int64_t qi_sb, qi_sh, qi_st;
+  const void* ki;       // [B, tk, 128]
+  int64_t ki_sb, ki_st;
+  const float* wi;      // [B, Hi, tq]
+  int32_t Hi, topk;
+  float* scores;        // workspace [B, tq, tk]
+  int32_t* list;        // [B, tq, topk] kept token indices, ascending
+  int32_t* count;       // [B, tq]
+};
+hipError_t launch_dsa_decode(const DsaArgs& a, hipStream_t s);
+
 constexpr int kMlaMaxSplits = 256;  // splits per sequence the merge accepts
 hipError_t launch_mla_decode(const MlaArgs& a, hipStream_t s);
 hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t s);

@@ -249,3 +249,40 @@ def mla_cache(B=64, H=16, lengths=None, lo=1024, hi=32768, tq=1, rank=512, rope=
     w_uk = (normal((H, rank, nope), seed + SEED_V) / math.sqrt(nope)).to(dtype)
     w_uv = (normal((H, rank, dv), seed + SEED_V + 100) / math.sqrt(rank)).to(dtype)
     return MlaCache(q_nope, q_rope, c_kv, k_rope, w_uk, w_uv, L)
+
+
+@dataclass
+class DsaInputs:
+    """A KV cache for token top-k sparse decode: q [B, Hq, tq, d], k, v [B, Hkv, cap, d]
+    (rows 0..L_b + tq - 1 drawn, the rest zero), the indexer's qi [B, Hi, tq, di] and
+    ki [B, cap, di] (N(0,1)) and head weights wi [B, Hi, tq] (N(0, 1/Hi)), cache_off = L_b."""
+
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    qi: torch.Tensor
+    ki: torch.Tensor
+    wi: torch.Tensor
+    sink: torch.Tensor
+    cache_off: torch.Tensor
+
+
+def dsa_inputs(B=64, Hq=32, Hkv=8, tq=1, lengths=None, lo=1024, hi=32768, Hi=64, d=128, di=128, seed=0,
+               dtype=torch.bfloat16) -> DsaInputs:
+    L = cache_lengths(B, lo, hi, seed) if lengths is None else torch.tensor(lengths, dtype=torch.int32)
+    cap = int(L.max()) + tq
+    k = torch.zeros((B, Hkv, cap, d), dtype=dtype)
+    v = torch.zeros((B, Hkv, cap, d), dtype=dtype)
+    ki = torch.zeros((B, cap, di), dtype=dtype)
+    gk = torch.Generator().manual_seed(seed + SEED_K)
+    gv = torch.Generator().manual_seed(seed + SEED_V)
+    for b in range(B):
+        n = int(L[b]) + tq
+        k[b, :, :n] = torch.randn((Hkv, n, d), generator=gk).to(dtype)
+        v[b, :, :n] = torch.randn((Hkv, n, d), generator=gv).to(dtype)
+        ki[b, :n] = torch.randn((n, di), generator=gk).to(dtype)
+    q = normal((B, Hq, tq, d), seed + SEED_Q, dtype)
+    qi = normal((B, Hi, tq, di), seed + SEED_Q + 100, dtype)
+    wi = normal((B, Hi, tq), seed + SEED_Q + 200) / math.sqrt(Hi)
+    sink = normal((Hq,), seed + SEED_SINK)
+    return DsaInputs(q, k, v, qi, ki, wi, sink, L)
