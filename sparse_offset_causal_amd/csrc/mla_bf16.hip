@@ -16,9 +16,9 @@
 //                           from an atomic queue; the 16 rows (heads x query tokens) are the N
 //                           columns of the MFMAs.  The four waves share the ring: each loads a
 //                           quarter of every block, computes the (cheap) scores in full and
-//                           a quarter of the 512-dim latent output.  Latent rows stream HBM -> LDS (buffer loads with the
-//                           LDS bit, 16-key blocks, a 4-stage ring, 16-byte chunks XOR-swizzled
-//                           by key); S^T = [C, R] [q_lat, q_rope]^T with
+//                           a quarter of the 512-dim latent output.  Latent rows go HBM ->
+//                           registers (two 16-key blocks ahead) -> LDS (a 2-stage ring,
+//                           16-byte chunks XOR-swizzled by key); S^T = [C, R] [q_lat, q_rope]^T with
 //                           v_mfma_f32_16x16x32_bf16 over 576 dims; online softmax in the log2
 //                           domain; O^T += C^T P^T with v_mfma_f32_16x16x16bf16_1k, C read
 //                           transposed by ds_read_b64_tr_b16.  Each item's unnormalised
@@ -37,7 +37,7 @@ namespace {
 
 constexpr int MR = kMlaRank, MDR = kMlaRope, MDN = kMlaNope, MDV = kMlaV;
 constexpr int MKB = 16;                      // keys per block
-constexpr int MNST = 4;                      // ring stages (3 blocks in flight)
+constexpr int MNST = 2;                      // LDS stages = register buffers; 2 blocks in flight
 constexpr int LAT_STAGE = MKB * MR;          // latent elements of one stage (16 KB)
 constexpr int ROPE_STAGE = MKB * MDR;        // rope elements of one stage (2 KB)
 constexpr int MSTAGE = LAT_STAGE + ROPE_STAGE;
@@ -161,20 +161,30 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) m
     const bf16_t* rb = (const bf16_t*)a.k_rope + b * a.r_sb;
     const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc((void*)cb, (short)0, (int)(ks1 * crow), 0x00020000);
     const __amdgpu_buffer_rsrc_t rrs = __builtin_amdgcn_make_buffer_rsrc((void*)rb, (short)0, (int)(ks1 * rrow), 0x00020000);
-    const uint32_t rope_v = rope_key * rrow + (uint32_t)(((lane & 7) ^ (rope_key & 7)) << 4);
-    auto issue = [&](int n, auto stage_tag) __attribute__((always_inline)) {
-      constexpr int ST = decltype(stage_tag)::value;
+    const uint32_t rope_v = rope_key * rrow + (uint32_t)(16 * (lane & 7));
+    // register staging of one block: latent rows 4 wave + i (lane: 16-byte chunk `lane`),
+    // rope keys 4 wave + lane/8 (lanes < 32: chunk lane & 7)
+    u32x4 stg[MNST][5];
+    auto issue = [&](int n, auto buf_tag) __attribute__((always_inline)) {
+      constexpr int BUF = decltype(buf_tag)::value;
       const uint32_t k0 = (uint32_t)(ks0 + n * MKB);
-      bf16_t* lat = lds + ST * MSTAGE;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        stg[BUF][i] = __builtin_amdgcn_raw_buffer_load_b128(crs, (uint32_t)(4 * wave + i) * crow + (uint32_t)(16 * lane),
+                                                            k0 * crow, 0);
+      if (lane < 32) stg[BUF][4] = __builtin_amdgcn_raw_buffer_load_b128(rrs, rope_v, k0 * rrow, 0);
+    };
+    // registers -> LDS stage, XOR-swizzled in 16-byte chunks by key
+    auto store = [&](auto buf_tag) __attribute__((always_inline)) {
+      constexpr int BUF = decltype(buf_tag)::value;
+      bf16_t* lat = lds + BUF * MSTAGE;
       bf16_t* rop = lat + LAT_STAGE;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int key = 4 * wave + i;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(crs, (lds_void_ptr)(lat + key * 512), 16,
-                                                 (uint32_t)((lane ^ key) << 4), (k0 + key) * crow, 0, 0);
+        *(u32x4*)(lat + key * 512 + ((lane ^ key) << 3)) = stg[BUF][i];
       }
-      if (lane < 32)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rrs, (lds_void_ptr)(rop + wave * 256), 16, rope_v, k0 * rrow, 0, 0);
+      if (lane < 32) *(u32x4*)(rop + rope_key * 64 + (((lane & 7) ^ (rope_key & 7)) << 3)) = stg[BUF][4];
     };
 
     // query fragments (B operand of S^T): dims 32ks + 8G .. +7 of row rho; 16 latent steps, 2 rope steps
@@ -192,7 +202,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) m
 
     if (nblk > 0) issue(0, std::integral_constant<int, 0>{});
     if (nblk > 1) issue(1, std::integral_constant<int, 1>{});
-    if (nblk > 2) issue(2, std::integral_constant<int, 2>{});
 
     f32x4 oacc[8];
 #pragma unroll
@@ -201,13 +210,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) m
 
     auto step = [&](int n, auto stage_tag) __attribute__((always_inline)) {
       constexpr int ST = decltype(stage_tag)::value;
-      // blocks n+1, n+2 (issued earlier) may stay in flight; block n must have landed everywhere
-      const int ahead = min(nblk - 1 - n, MNST - 2);
-      if (ahead >= 2) wait_wave_blocks<2>();
-      else if (ahead == 1) wait_wave_blocks<1>();
+      // block n+1 (issued earlier) may stay in flight; block n's registers must have landed
+      if (n + 1 < nblk) wait_wave_blocks<1>();
       else wait_wave_blocks<0>();
-      __syncthreads();  // block n is in LDS, and every wave is done with block n-1's stage
-      if (n + MNST - 1 < nblk) issue(n + MNST - 1, std::integral_constant<int, (ST + MNST - 1) % MNST>{});
+      store(std::integral_constant<int, ST>{});  // stage ST held block n-2: every wave finished it before barrier n-1
+      if (n + 2 < nblk) issue(n + 2, std::integral_constant<int, ST>{});  // the registers just stored
+      __syncthreads();  // every wave's part of block n is in LDS
       const bf16_t* lat = lds + ST * MSTAGE;
       const bf16_t* rop = lat + LAT_STAGE;
 
@@ -262,8 +270,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) m
     for (int n = 0; n < nblk; n += MNST) {
       step(n, std::integral_constant<int, 0>{});
       if (n + 1 < nblk) step(n + 1, std::integral_constant<int, 1>{});
-      if (n + 2 < nblk) step(n + 2, std::integral_constant<int, 2>{});
-      if (n + 3 < nblk) step(n + 3, std::integral_constant<int, 3>{});
     }
 
     // the row's sum over the 4 lanes that share it
