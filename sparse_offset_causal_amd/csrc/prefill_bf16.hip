@@ -27,9 +27,9 @@
 //   flight while tile n is consumed, with one barrier per tile.  Both tiles are row-major
 //   with a 16-byte-chunk XOR swizzle applied on the load side.  K is read as the MFMA A
 //   operand with ds_read_b128 (chunk' = chunk ^ (row & 15): 16 consecutive keys hit 16
-//   distinct bank groups).  V is read already transposed with ds_read_b64_tr_b16 (each
-//   16-lane group reads a 4-key x 16-column block; chunk' = chunk ^ 4*(row & 3) makes the
-//   two groups of a half-wave cover all 64 banks once).  The loads are buffer loads whose
+//   distinct bank groups), four MFMA steps ahead of use.  V is read already transposed with
+//   ds_read_b64_tr_b16 (each 16-lane group reads a 4-key x 16-column block; chunk' = chunk ^
+//   4*(row & 3) makes the two groups of a half-wave cover all 64 banks once).  The loads are buffer loads whose
 //   range ends at the last row any query of the workgroup may see: later rows read as zero
 //   and are masked.  All LDS and DMA addressing is per-lane offsets fixed at kernel start
 //   plus immediates or one scalar per tile.
@@ -55,6 +55,7 @@ constexpr int NTHR = 256;
 constexpr int TILE_ELEMS = KT * D;              // one K or V tile, 16 KB
 constexpr int BUF_ELEMS = 2 * TILE_ELEMS;       // K then V
 constexpr float RESCALE_SLACK = 8.0f;           // log2 units the running max may lag
+constexpr int KAHEAD = 4;                       // K fragment reads in flight ahead of the S MFMAs
 
 typedef short s16x4 __attribute__((__vector_size__(8)));
 typedef short s16x8 __attribute__((__vector_size__(16)));
@@ -218,10 +219,24 @@ prefill_bf16_d128(AttnArgs a) {
     f32x16 s0, s1;
 #pragma unroll
     for (int v = 0; v < 16; ++v) { s0[v] = 0.f; s1[v] = 0.f; }
+    // K fragments are read KAHEAD steps ahead of the MFMAs that use them; the scheduling
+    // barriers keep the compiler from sinking the reads back next to their uses.
+    bf16x8 kf0[8], kf1[8];
+#pragma unroll
+    for (int ks = 0; ks < KAHEAD; ++ks) {
+      kf0[ks] = *(const bf16x8*)(kt + koff[ks]);
+      kf1[ks] = *(const bf16x8*)(kt + 32 * D + koff[ks]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      s0 = mfma32x32x16(*(const bf16x8*)(kt + koff[ks]), qf[ks], s0);
-      s1 = mfma32x32x16(*(const bf16x8*)(kt + 32 * D + koff[ks]), qf[ks], s1);
+      if (ks + KAHEAD < 8) {
+        kf0[ks + KAHEAD] = *(const bf16x8*)(kt + koff[ks + KAHEAD]);
+        kf1[ks + KAHEAD] = *(const bf16x8*)(kt + 32 * D + koff[ks + KAHEAD]);
+      }
+      s0 = mfma32x32x16(kf0[ks], qf[ks], s0);
+      s1 = mfma32x32x16(kf1[ks], qf[ks], s1);
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (need_mask) {
       asm volatile("");  // keeps this a branch: only tiles on a causal or window edge pay for it
