@@ -11,10 +11,12 @@
 //   dsa_indexer_kernel  one wave per (sequence, query token, 256 tokens): scores^T = Ki Qi^T
 //                       with v_mfma_f32_16x16x32_bf16 (16 tokens x 16 indexer heads per MFMA),
 //                       ReLU and the head weights in fp32, the sum over heads in a fixed order
-//   dsa_topk_kernel     one 1024-thread workgroup per (sequence, query token): 4-pass radix
-//                       select of the k-th largest score on order-preserving 32-bit keys, then
-//                       an index-ordered compaction (ties at the threshold: lowest indices)
-//                       into an ascending list
+//   dsa_topk_kernel     one 1024-thread workgroup per (sequence, query token): radix select of
+//                       the k-th largest score on order-preserving 32-bit keys (digits of 12,
+//                       12 and 8 bits; the first histogram is built while the keys are staged
+//                       in LDS), then an index-ordered compaction (ties at the threshold:
+//                       lowest indices) into an ascending list, one contiguous token segment
+//                       per wave
 //   dsa_split_kernel    split-KV decode over the kept list: one wave per (sequence, KV head,
 //                       query token, split of the list); K rows are gathered by index straight
 //                       into registers and V rows by index into LDS (buffer loads with the LDS
@@ -115,112 +117,170 @@ __global__ void __launch_bounds__(64) dsa_indexer_kernel(DsaArgs A) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Wave-wide search in descending order over 64 lanes x 4 bins (lane l: bins 4l..4l+3).
-__device__ void locate_digit(const unsigned* hist, unsigned rank, unsigned* digit, unsigned* rank_in) {
+// Inclusive suffix sum over the lanes of a wave (lane l gets the sum over lanes >= l).
+__device__ __forceinline__ unsigned wave_suffix_sum(unsigned x) {
   const int lane = threadIdx.x & 63;
-  const unsigned c = hist[4 * lane] + hist[4 * lane + 1] + hist[4 * lane + 2] + hist[4 * lane + 3];
-  unsigned s = c;  // inclusive suffix sum over lanes >= this one
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    const unsigned y = __shfl_down(s, o, 64);
-    if (lane + o < 64) s += y;
+    const unsigned y = __shfl_down(x, o, 64);
+    if (lane + o < 64) x += y;
   }
+  return x;
+}
+
+// One wave finds the bin holding descending rank `rank` of an NB-bin histogram and the rank
+// within that bin: lane l first sums bins [G l, G l + G), then the chosen group's G bins are
+// searched one per lane (G = 64) or in turn (G = 4).
+template <int NB>
+__device__ void locate_digit(const unsigned* hist, unsigned rank, unsigned* digit, unsigned* rank_in) {
+  constexpr int G = NB / 64;
+  const int lane = threadIdx.x & 63;
+  unsigned c = 0;
+#pragma unroll
+  for (int j = 0; j < G; ++j) c += hist[G * lane + j];
+  const unsigned s = wave_suffix_sum(c);
   const unsigned ab = s - c;
   const unsigned long long own = __ballot(ab <= rank && rank < s);
   const int L = own ? __ffsll(own) - 1 : 0;
-  unsigned r = rank - __shfl(ab, L, 64);
-  int e = 3;
-  for (; e > 0; --e) {
-    const unsigned h = hist[4 * L + e];
-    if (r < h) break;
-    r -= h;
+  unsigned r = rank - (unsigned)__builtin_amdgcn_readlane((int)ab, L);
+  if constexpr (G == 64) {
+    const unsigned h = hist[G * L + lane];
+    const unsigned s2 = wave_suffix_sum(h);
+    const unsigned ab2 = s2 - h;
+    const unsigned long long own2 = __ballot(ab2 <= r && r < s2);
+    const int j = own2 ? __ffsll(own2) - 1 : 0;
+    *digit = G * L + j;
+    *rank_in = r - (unsigned)__builtin_amdgcn_readlane((int)ab2, j);
+  } else {
+    int e = G - 1;
+    for (; e > 0; --e) {
+      const unsigned h = hist[G * L + e];
+      if (r < h) break;
+      r -= h;
+    }
+    *digit = G * L + e;
+    *rank_in = r;
   }
-  *digit = 4 * L + e;
-  *rank_in = r;
-}
-
-// Block-wide exclusive prefix count of `flag` (1024 threads) plus the block total.
-__device__ __forceinline__ unsigned block_prefix(bool flag, unsigned* wsum, unsigned* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const unsigned long long bal = __ballot(flag);
-  const unsigned before = __popcll(bal & ((1ull << lane) - 1ull));
-  if (lane == 0) wsum[wave] = __popcll(bal);
-  __syncthreads();
-  unsigned wbase = 0, tot = 0;
-  for (int w = 0; w < 16; ++w) {
-    const unsigned c = wsum[w];
-    if (w < wave) wbase += c;
-    tot += c;
-  }
-  __syncthreads();
-  *total = tot;
-  return wbase + before;
 }
 
 constexpr int TOPK_LDS = 32768;  // scores of up to this many visible tokens are staged in LDS
+constexpr int TOPK_BINS = 4096;  // digits of 12, 12 and 8 bits
 
 __global__ void __launch_bounds__(1024) dsa_topk_kernel(DsaArgs A) {
   const AttnArgs& a = A.at;
-  __shared__ unsigned hist[256];
+  __shared__ unsigned hist[TOPK_BINS];
   __shared__ unsigned su[2];
-  __shared__ unsigned wsum[16];
+  __shared__ unsigned wcnt[2][16];
   __shared__ uint32_t keys[TOPK_LDS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t = blockIdx.x % a.tq, b = blockIdx.x / a.tq;
   const int n_vis = min(a.tk, seq_off(a, b) + t + 1);
   const int K = A.topk;
   int32_t* lst = A.list + ((int64_t)b * a.tq + t) * K;
   if (n_vis <= K) {  // every visible token is kept
-    for (int j = threadIdx.x; j < n_vis; j += 1024) lst[j] = j;
-    if (threadIdx.x == 0) A.count[b * a.tq + t] = n_vis;
+    for (int j = tid; j < n_vis; j += 1024) lst[j] = j;
+    if (tid == 0) A.count[b * a.tq + t] = n_vis;
     return;
   }
   const float* sc = A.scores + ((int64_t)b * a.tq + t) * a.tk;
   const bool staged = n_vis <= TOPK_LDS;
-  if (staged)
-    for (int i = threadIdx.x; i < n_vis; i += 1024) keys[i] = f32_order_key(sc[i]);
   auto key_at = [&](int i) __attribute__((always_inline)) { return staged ? keys[i] : f32_order_key(sc[i]); };
-  // radix select of the key at descending rank K - 1
-  unsigned prefix = 0, pmask = 0, rank = (unsigned)(K - 1);
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    if (threadIdx.x < 256) hist[threadIdx.x] = 0;
-    __syncthreads();
-    for (int i = threadIdx.x; i < n_vis; i += 1024) {
-      const uint32_t key = key_at(i);
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+
+  // Radix select of the key at descending rank K - 1: the histogram of the top 12 bits is
+  // built while the keys are staged, then bits 19..8 and 7..0 among the keys that share the
+  // digits chosen so far.
+  for (int i = tid; i < TOPK_BINS; i += 1024) hist[i] = 0;
+  __syncthreads();
+  for (int i0 = tid; i0 < n_vis; i0 += 4 * 1024) {
+    uint32_t kv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + 1024 * u;
+      kv[u] = i < n_vis ? f32_order_key(sc[i]) : 0u;
     }
-    __syncthreads();
-    if (threadIdx.x < 64) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + 1024 * u;
+      if (i < n_vis) {
+        if (staged) keys[i] = kv[u];
+        atomicAdd(&hist[kv[u] >> 20], 1u);
+      }
+    }
+  }
+  __syncthreads();
+  unsigned prefix = 0, pmask = 0, rank = (unsigned)(K - 1);
+  auto choose = [&](auto nb_tag, int shift, unsigned dmask) __attribute__((always_inline)) {
+    constexpr int NB = decltype(nb_tag)::value;
+    if (wave == 0) {
       unsigned dg, r;
-      locate_digit(hist, rank, &dg, &r);
-      if (threadIdx.x == 0) {
-        su[0] = prefix | (dg << shift);
+      locate_digit<NB>(hist, rank, &dg, &r);
+      if (lane == 0) {
+        su[0] = dg;
         su[1] = r;
       }
     }
     __syncthreads();
-    prefix = su[0];
+    prefix |= su[0] << shift;
+    pmask |= dmask << shift;
     rank = su[1];
-    pmask |= 255u << shift;
+  };
+  auto count_digit = [&](int shift, unsigned dmask, int nb) __attribute__((always_inline)) {
+    for (int i = tid; i < nb; i += 1024) hist[i] = 0;
     __syncthreads();
-  }
-  // keys above the threshold, then the first rank + 1 keys equal to it in token order
+    for (int i = tid; i < n_vis; i += 1024) {
+      const uint32_t key = key_at(i);
+      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1u);
+    }
+    __syncthreads();
+  };
+  choose(std::integral_constant<int, 4096>{}, 20, 0xfffu);
+  count_digit(8, 0xfffu, 4096);
+  choose(std::integral_constant<int, 4096>{}, 8, 0xfffu);
+  count_digit(0, 0xffu, 256);
+  choose(std::integral_constant<int, 256>{}, 0, 0xffu);
+
+  // Ordered compaction: keys above the threshold, then the first rank + 1 keys equal to it in
+  // token order.  Wave w owns a contiguous segment of tokens; one count pass and one barrier
+  // give every wave its output offset, a second pass writes the indices in order.
   const uint32_t tau = prefix;
   const unsigned need_eq = rank + 1;
-  unsigned base = 0, eq_base = 0;
-  for (int c0 = 0; c0 < n_vis; c0 += 1024) {
-    const int i = c0 + threadIdx.x;
-    const uint32_t key = i < n_vis ? key_at(i) : 0u;
-    const bool gt = i < n_vis && key > tau;
-    const bool eq = i < n_vis && key == tau;
-    unsigned eq_tot, keep_tot;
-    const unsigned eq_rank = eq_base + block_prefix(eq, wsum, &eq_tot);
-    const bool keep = gt || (eq && eq_rank < need_eq);
-    const unsigned pos = base + block_prefix(keep, wsum, &keep_tot);
-    if (keep) lst[pos] = i;
-    base += keep_tot;
-    eq_base += eq_tot;
+  const int seg = ((n_vis + 16 * 64 - 1) / (16 * 64)) * 64;
+  const int w0 = wave * seg, w1 = min(w0 + seg, n_vis);
+  unsigned gt_c = 0, eq_c = 0;
+  for (int c0 = w0; c0 < w0 + seg; c0 += 64) {
+    const int i = c0 + lane;
+    const bool in = i < w1;
+    const uint32_t key = in ? key_at(i) : 0u;
+    gt_c += (unsigned)__popcll(__ballot(in && key > tau));
+    eq_c += (unsigned)__popcll(__ballot(in && key == tau));
   }
-  if (threadIdx.x == 0) A.count[b * a.tq + t] = K;
+  if (lane == 0) {
+    wcnt[0][wave] = gt_c;
+    wcnt[1][wave] = eq_c;
+  }
+  __syncthreads();
+  unsigned eq_seen = 0, out = 0;
+  for (int w = 0; w < wave; ++w) {
+    const unsigned g = wcnt[0][w], e = wcnt[1][w];
+    const unsigned left = need_eq > eq_seen ? need_eq - eq_seen : 0u;
+    out += g + (e < left ? e : left);
+    eq_seen += e;
+  }
+  const unsigned long long lt_mask = (1ull << lane) - 1ull;
+  for (int c0 = w0; c0 < w0 + seg; c0 += 64) {
+    const int i = c0 + lane;
+    const bool in = i < w1;
+    const uint32_t key = in ? key_at(i) : 0u;
+    const bool gt = in && key > tau, eq = in && key == tau;
+    const unsigned long long beq = __ballot(eq);
+    const bool keep = gt || (eq && eq_seen + (unsigned)__popcll(beq & lt_mask) < need_eq);
+    const unsigned long long bk = __ballot(keep);
+    const unsigned pos = out + (unsigned)__popcll(bk & lt_mask);
+    if (keep && pos < (unsigned)K) lst[pos] = i;
+    eq_seen += (unsigned)__popcll(beq);
+    out += (unsigned)__popcll(bk);
+  }
+  if (tid == 0) A.count[b * a.tq + t] = K;
 }
 
 // ---------------------------------------------------------------------------------------

@@ -11,7 +11,7 @@ import torch
 
 import synth
 from oracle import attend
-from oracle.dsa import sparse_attend
+from oracle.dsa import indexer_scores, sparse_attend, topk_keep
 from sparse_offset_causal_amd import AttnError, attn_decode, attn_dsa_decode
 from tests.gpu_helpers import BF16_TOL, announce, dev, host64, max_abs, require_gpu
 
@@ -89,3 +89,34 @@ def test_dsa_decode_rejects_bad_index_heads():
     x = synth.dsa_inputs(B=1, Hq=8, Hkv=2, lengths=[10], Hi=8, seed=1)
     with pytest.raises(AttnError, match="index_heads"):
         run(x, 4)
+
+
+def test_dsa_topk_exact_ties_keep_lowest_indices():
+    """600 tokens share one indexer key row (bitwise-equal scores on both sides); 30 tokens
+    carry twice that row (strictly larger scores).  top-k then cuts inside the tie group, and
+    the kept set must be the larger tokens plus the lowest-indexed tied ones, exactly; the tie
+    group spans the token segments of several waves of the selection kernel."""
+    announce("dsa top-k exact ties")
+    x = synth.dsa_inputs(B=1, Hq=8, Hkv=2, lengths=[5000], Hi=16, seed=21)
+    # a key row along the positively weighted indexer queries scores far above random rows
+    w, qv = x.wi[0, :, 0].float(), x.qi[0, :, 0].float()
+    dirn = (w.clamp(min=0)[:, None] * qv).sum(0)
+    tie_row = (dirn / dirn.norm() * 4 * 128 ** 0.5).to(x.ki.dtype)
+    tie_score = indexer_scores(x.qi, tie_row.view(1, 1, -1), x.wi)[0, 0, 0]
+    assert tie_score > 0
+    tied = torch.arange(200, 200 + 3 * 600, 3)
+    top = torch.arange(2500, 2530)
+    x.ki[0, tied] = tie_row
+    x.ki[0, top] = (tie_row.float() * 2).to(x.ki.dtype)  # exact in bf16
+    scores = indexer_scores(x.qi, x.ki, x.wi)[0, 0, :5001]
+    n_gt = int((scores > tie_score).sum())
+    assert int((scores == tie_score).sum()) == 600 and n_gt == 30
+    topk = n_gt + 250
+    keep = topk_keep(indexer_scores(x.qi, x.ki, x.wi), topk, x.cache_off)
+    want = np.nonzero(keep[0, 0])[0]
+    assert np.array_equal(want[np.isin(want, tied.numpy())], tied.numpy()[:250])
+    o, kl, kc = run(x, topk)
+    got = kl.cpu().numpy()[0, 0, :int(kc[0, 0])]
+    assert np.array_equal(got, want)
+    ref = sparse_attend(x.q, x.k, x.v, x.qi, x.ki, x.wi, topk, cache_off=x.cache_off, sink=x.sink)
+    assert max_abs(o, ref) <= BF16_TOL
