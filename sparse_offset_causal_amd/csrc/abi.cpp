@@ -549,6 +549,7 @@ int attn_dsa_decode(const attn_shape_t* shape, const void* q, attn_strides_t q_s
   A.scores = reinterpret_cast<float*>(ws + L.scores);
   A.list = kept_list ? kept_list : reinterpret_cast<int32_t*>(ws + L.list);
   A.count = kept_count ? kept_count : reinterpret_cast<int32_t*>(ws + L.count);
+  A.idx_waves = 12 * device_cus();  // three single-wave workgroups per SIMD (148 VGPRs each)
   return finish(soc::launch_dsa_decode(A, stream), stream, "attn_dsa_decode launch");
 }
 

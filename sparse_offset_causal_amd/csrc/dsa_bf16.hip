@@ -8,9 +8,12 @@
 // visible); equal scores go to the lower token index.  Every head of the query token attends
 // over the same kept set.
 //
-//   dsa_indexer_kernel  one wave per (sequence, query token, 256 tokens): scores^T = Ki Qi^T
-//                       with v_mfma_f32_16x16x32_bf16 (16 tokens x 16 indexer heads per MFMA),
-//                       ReLU and the head weights in fp32, the sum over heads in a fixed order
+//   dsa_indexer_kernel  a fixed grid of single-wave workgroups (three per SIMD), each scoring
+//                       an equal share of all 16-token blocks of all (sequence, query token)
+//                       rows, so that every wave ends at about the same time: scores^T =
+//                       Ki Qi^T with v_mfma_f32_16x16x32_bf16 (16 tokens x 16 indexer heads per
+//                       MFMA), ReLU and the head weights in fp32, the sum over heads in a fixed
+//                       order (DPP within each 16-lane row)
 //   dsa_topk_kernel     one 1024-thread workgroup per (sequence, query token): radix select of
 //                       the k-th largest score on order-preserving 32-bit keys (digits of 12,
 //                       12 and 8 bits; the first histogram is built while the keys are staged
@@ -48,6 +51,19 @@ __device__ __forceinline__ f32x4 mfma16k32(bf16x8 a, bf16x8 b, f32x4 c) {
   // lane l: A[l%16][8(l/16)+e], B[8(l/16)+e][l%16], D[4(l/16)+v][l%16]
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+// Sum over each row of 16 lanes with DPP (xor 1, xor 2, then the mirrors within 8 and 16
+// lanes), the same pairing as a butterfly on lane ^ 1, 2, 4, 8.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_f32<0xb1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_f32<0x4e>(x);   // quad_perm [2,3,0,1]
+  x += dpp_f32<0x141>(x);  // row_half_mirror
+  x += dpp_f32<0x140>(x);  // row_mirror
+  return x;
+}
 __device__ __forceinline__ uint32_t f32_order_key(float x) {
   const uint32_t u = __builtin_bit_cast(uint32_t, x);
   return (u >> 31) ? ~u : (u | 0x80000000u);
@@ -55,64 +71,121 @@ __device__ __forceinline__ uint32_t f32_order_key(float x) {
 __device__ __forceinline__ int seq_off(const AttnArgs& a, int b) { return a.cache_off ? a.cache_off[b] : a.tk - a.tq; }
 
 // ---------------------------------------------------------------------------------------
+// Sum and inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_sum_i(int x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+__device__ __forceinline__ int wave_incl_prefix_i(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
 __global__ void __launch_bounds__(64) dsa_indexer_kernel(DsaArgs A) {
   const AttnArgs& a = A.at;
   const int lane = threadIdx.x, G = lane >> 4, i16 = lane & 15;
-  const int nch = (a.tk + 255) / 256;
-  int bid = blockIdx.x;
-  const int ch = bid % nch;
-  bid /= nch;
-  const int t = bid % a.tq, b = bid / a.tq;
-  const int n_vis = min(a.tk, seq_off(a, b) + t + 1);
-  const int s0 = ch * 256;
-  if (s0 >= n_vis) return;
-  const int nhb = A.Hi / 16;
-  bf16x8 qb[4][4];
-  float w[4];
-  const u32x4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int hb = 0; hb < 4; ++hb) {
-    const int head = 16 * hb + i16;
-    const bool ok = hb < nhb;
-    const bf16_t* qp = (const bf16_t*)A.qi + b * A.qi_sb + head * A.qi_sh + t * A.qi_st;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qb[hb][ks] = ok ? *(const bf16x8*)(qp + 32 * ks + 8 * G) : as_bf16x8(z);
-    w[hb] = ok ? A.wi[((int64_t)b * A.Hi + head) * a.tq + t] : 0.f;
+  const int rows = a.B * a.tq;
+  // Row r = b * tq + t has nb(r) = ceil(n_vis / 16) blocks of 16 tokens; the blocks of all
+  // rows, in row order, are split evenly over the waves of the grid.
+  auto row_blocks = [&](int r) __attribute__((always_inline)) -> int {
+    if (r >= rows) return 0;
+    const int b = r / a.tq, t = r - b * a.tq;
+    return (min(a.tk, seq_off(a, b) + t + 1) + 15) >> 4;
+  };
+  int total = 0;
+  for (int r0 = 0; r0 < rows; r0 += 64) total += wave_sum_i(row_blocks(r0 + lane));
+  total = __builtin_amdgcn_readfirstlane(total);
+  const int W = gridDim.x, wid = blockIdx.x;
+  const int lo = (int)((int64_t)total * wid / W), hi = (int)((int64_t)total * (wid + 1) / W);
+  if (lo >= hi) return;
+  int row = 0, rstart = 0;  // the row holding block lo and the global index of its first block
+  for (int r0 = 0, base = 0; r0 < rows; r0 += 64) {
+    const int nb = row_blocks(r0 + lane);
+    const int incl = base + wave_incl_prefix_i(nb);
+    const unsigned long long own = __ballot(nb > 0 && incl - nb <= lo && lo < incl);
+    if (own) {
+      const int L = __ffsll(own) - 1;
+      row = r0 + L;
+      rstart = __builtin_amdgcn_readlane(incl - nb, L);
+      break;
+    }
+    base = __builtin_amdgcn_readlane(incl, 63);
   }
+  row = __builtin_amdgcn_readfirstlane(row);
+  rstart = __builtin_amdgcn_readfirstlane(rstart);
+
+  const int nhb = A.Hi / 16;
   const uint32_t row_bytes = (uint32_t)A.ki_st * 2u;
-  const bf16_t* kp = (const bf16_t*)A.ki + b * A.ki_sb;
-  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kp, (short)0, (int)(n_vis * row_bytes), 0x00020000);
-  float* out = A.scores + ((int64_t)b * a.tq + t) * a.tk;
-  for (int blk = 0; blk < 16; ++blk) {
-    const int tok0 = s0 + 16 * blk;
-    if (tok0 >= n_vis) break;
-    bf16x8 af[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      af[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                                              krs, (uint32_t)(tok0 + i16) * row_bytes + (uint32_t)(64 * ks + 16 * G), 0, 0));
-    float part[4] = {0.f, 0.f, 0.f, 0.f};
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  for (int g = lo; g < hi;) {
+    const int b = __builtin_amdgcn_readfirstlane(row / a.tq);
+    const int t = __builtin_amdgcn_readfirstlane(row - b * a.tq);
+    const int n_vis = __builtin_amdgcn_readfirstlane(min(a.tk, seq_off(a, b) + t + 1));
+    const int nb_row = (n_vis + 15) >> 4;
+    bf16x8 qb[4][4];
+    float w[4];
 #pragma unroll
     for (int hb = 0; hb < 4; ++hb) {
-      if (hb >= nhb) break;  // uniform
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      const int head = 16 * hb + i16;
+      const bool ok = hb < nhb;
+      const bf16_t* qp = (const bf16_t*)A.qi + b * A.qi_sb + head * A.qi_sh + t * A.qi_st;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) acc = mfma16k32(af[ks], qb[hb][ks], acc);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) part[v] = fmaf(w[hb], fmaxf(acc[v], 0.f), part[v]);
+      for (int ks = 0; ks < 4; ++ks) qb[hb][ks] = ok ? *(const bf16x8*)(qp + 32 * ks + 8 * G) : as_bf16x8(z);
+      w[hb] = ok ? A.wi[((int64_t)b * A.Hi + head) * a.tq + t] : 0.f;
     }
-    // lane (G, i16): tokens 4G + v, indexer head i16 of each block; sum over the 16 heads
+    const bf16_t* kp = (const bf16_t*)A.ki + b * A.ki_sb;
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kp, (short)0, (int)(n_vis * row_bytes), 0x00020000);
+    float* out = A.scores + ((int64_t)b * a.tq + t) * a.tk;
+    const int j0 = g - rstart, j1 = min(nb_row, hi - rstart);  // this wave's blocks of the row
+    auto load = [&](bf16x8* af, int j) __attribute__((always_inline)) {
+      const int tok0 = 16 * j;
 #pragma unroll
-    for (int v = 0; v < 4; ++v)
+      for (int ks = 0; ks < 4; ++ks)
+        af[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                                krs, (uint32_t)(tok0 + i16) * row_bytes + (uint32_t)(64 * ks + 16 * G), 0, 0));
+    };
+    auto score = [&](const bf16x8* af, int j) __attribute__((always_inline)) {
+      const int tok0 = 16 * j;
+      float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int m = 1; m < 16; m <<= 1) part[v] += __shfl_xor(part[v], m, 64);
-    if (i16 == 0) {
+      for (int hb = 0; hb < 4; ++hb) {
+        if (hb >= nhb) break;  // uniform
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int tok = tok0 + 4 * G + v;
-        if (tok < n_vis) out[tok] = part[v];
+        for (int ks = 0; ks < 4; ++ks) acc = mfma16k32(af[ks], qb[hb][ks], acc);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) part[v] = fmaf(w[hb], fmaxf(acc[v], 0.f), part[v]);
       }
+      // lane (G, i16): tokens 4G + v, indexer head i16 of each block; sum over the 16 heads
+#pragma unroll
+      for (int v = 0; v < 4; ++v) part[v] = row16_sum(part[v]);
+      if (i16 == 0) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int tok = tok0 + 4 * G + v;
+          if (tok < n_vis) out[tok] = part[v];
+        }
+      }
+    };
+    // the keys of block j + 1 are in flight while block j is scored
+    bf16x8 fa[4], fb[4];
+    load(fa, j0);
+    for (int j = j0; j < j1; j += 2) {
+      if (j + 1 < j1) load(fb, j + 1);
+      score(fa, j);
+      if (j + 1 >= j1) break;
+      if (j + 2 < j1) load(fa, j + 2);
+      score(fb, j + 1);
     }
+    g = rstart + j1;
+    rstart += nb_row;
+    ++row;
   }
 }
 
@@ -458,7 +531,7 @@ hipError_t launch_dsa_decode(const DsaArgs& A, hipStream_t s) {
   const AttnArgs& a = A.at;
   const int64_t rows = (int64_t)a.B * a.tq;
   if (rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(dsa_indexer_kernel, dim3((unsigned)(rows * ((a.tk + 255) / 256))), dim3(64), 0, s, A);
+  hipLaunchKernelGGL(dsa_indexer_kernel, dim3((unsigned)A.idx_waves), dim3(64), 0, s, A);
   hipLaunchKernelGGL(dsa_topk_kernel, dim3((unsigned)rows), dim3(1024), 0, s, A);
   hipLaunchKernelGGL(dsa_split_kernel, dim3((unsigned)(rows * a.Hkv * a.nsplit)), dim3(64), 0, s, A);
   // every split has a partial: the merge reads all nsplit of them (no offsets, tk = nsplit * split)

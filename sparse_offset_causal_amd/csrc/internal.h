@@ -125,6 +125,7 @@ struct DsaArgs {
   float* scores;        // workspace [B, tq, tk]
   int32_t* list;        // [B, tq, topk] kept token indices, ascending
   int32_t* count;       // [B, tq]
+  int32_t idx_waves;    // waves of the indexer grid (each scores an equal share of all blocks)
 };
 hipError_t launch_dsa_decode(const DsaArgs& a, hipStream_t s);
 
