@@ -216,31 +216,79 @@ decode_split_bf16_d128(AttnArgs a) {
   }
 }
 
+__device__ __forceinline__ float wave_max_f(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+__device__ __forceinline__ float wave_sum_f(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+// One wave per output row.  The splits' (max, sum) pairs are spread over the lanes (64 splits
+// per pass) and reduced across the wave; each split's weight 2^(m_s - M) / L is then taken
+// from its lane, and the partial outputs are summed with several loads in flight.
 template <typename OutT>
 __global__ void __launch_bounds__(64) decode_merge(AttnArgs a) {
   const int64_t rowid = blockIdx.x;
+  const int lane = threadIdx.x;
   const int r = (int)(rowid % a.tq);
   const int h = (int)((rowid / a.tq) % a.Hq);
   const int b = (int)(rowid / ((int64_t)a.tq * a.Hq));
   const int off = a.cache_off ? a.cache_off[b] : a.tk - a.tq;
   const int tkb = off + a.tq;
-  const int nsb = (tkb + a.split - 1) / a.split;
+  const int nsb = __builtin_amdgcn_readfirstlane((tkb + a.split - 1) / a.split);
   const float* pml = a.part + decode_o_floats(a) + rowid * a.nsplit * 2;
   const float* po = a.part + rowid * a.nsplit * a.d;
   float M = SOC_NEG_INF;
-  for (int s = 0; s < nsb; ++s) M = fmaxf(M, pml[2 * s]);
+  for (int s0 = 0; s0 < nsb; s0 += 64)
+    if (s0 + lane < nsb) M = fmaxf(M, pml[2 * (s0 + lane)]);
   const float sink_l2 = a.sink ? a.sink[h] * kLog2e : SOC_NEG_INF;
-  M = fmaxf(M, sink_l2);
+  M = fmaxf(wave_max_f(M), sink_l2);
   const float M_use = (M == SOC_NEG_INF) ? 0.f : M;
-  float L = fast_exp2(sink_l2 - M_use);
-  for (int s = 0; s < nsb; ++s) L += pml[2 * s + 1] * fast_exp2(pml[2 * s] - M_use);
+  float Lp = 0.f;
+  for (int s0 = 0; s0 < nsb; s0 += 64)
+    if (s0 + lane < nsb) Lp += pml[2 * (s0 + lane) + 1] * fast_exp2(pml[2 * (s0 + lane)] - M_use);
+  const float L = wave_sum_f(Lp) + fast_exp2(sink_l2 - M_use);
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  OutT* op = (OutT*)a.o + b * a.o_sb + h * a.o_sh + (int64_t)r * a.o_st;
-  for (int t = threadIdx.x; t < a.d; t += 64) {
-    float acc = 0.f;
-    for (int s = 0; s < nsb; ++s) acc += po[(int64_t)s * a.d + t] * fast_exp2(pml[2 * s] - M_use);
-    op[t] = (OutT)(acc * inv);
+  auto weight = [&](int wl_bits, int s) __attribute__((always_inline)) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(wl_bits, s));
+  };
+  // columns lane and lane + 64 (head_dim <= 128); every lane stays active through the split
+  // loop, so each split's weight can be read from its lane
+  const bool c0 = lane < a.d, c1 = lane + 64 < a.d;
+  float acc0 = 0.f, acc1 = 0.f;
+  for (int s0 = 0; s0 < nsb; s0 += 64) {
+    // lane j holds the weight 2^(m_s - M) of split s0 + j
+    const int wl = __builtin_bit_cast(int, s0 + lane < nsb ? fast_exp2(pml[2 * (s0 + lane)] - M_use) : 0.f);
+    const int n = min(64, nsb - s0);
+    const float* pp = po + (int64_t)s0 * a.d + lane;
+    int s = 0;
+    for (; s + 4 <= n; s += 4) {
+      float v0[4], v1[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        v0[u] = c0 ? pp[(int64_t)(s + u) * a.d] : 0.f;
+        v1[u] = c1 ? pp[(int64_t)(s + u) * a.d + 64] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float w = weight(wl, s + u);
+        acc0 += v0[u] * w;
+        acc1 += v1[u] * w;
+      }
+    }
+    for (; s < n; ++s) {
+      const float w = weight(wl, s);
+      if (c0) acc0 += pp[(int64_t)s * a.d] * w;
+      if (c1) acc1 += pp[(int64_t)s * a.d + 64] * w;
+    }
   }
+  OutT* op = (OutT*)a.o + b * a.o_sb + h * a.o_sh + (int64_t)r * a.o_st;
+  if (c0) op[lane] = (OutT)(acc0 * inv);
+  if (c1) op[lane + 64] = (OutT)(acc1 * inv);
 }
 
 }  // namespace
