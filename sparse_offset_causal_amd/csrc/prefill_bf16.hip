@@ -15,11 +15,12 @@
 //   lane owns one query row (lane % 32) and 16 keys per 32-key block: the row max and sum
 //   need one exchange between the two wave halves, and the output O^T = V^T P^T again
 //   leaves one row per lane, so the softmax rescale is a per-lane scalar.
-//   Masks are computed from indices only on tiles that cross a row's causal limit or
-//   window edge.  The online softmax runs in the log2 domain in fp32 with the scale folded
-//   into the exponent's FMA; the running max is only raised (and O, l rescaled) when a
-//   row's max grows by more than 2^8, so most tiles skip the rescale; P is rounded to bf16
-//   for the second MFMA; O accumulates in fp32 and is rounded to bf16 once at the end.
+//   Masks are computed from indices only on tiles that cross a row's causal limit, and
+//   separately only on tiles that cross a row's window edge.  The online softmax runs in
+//   the log2 domain in fp32 with the scale folded into the exponent's FMA; the running max
+//   is only raised (and O, l rescaled) when a row's max grows by more than 2^8, so most
+//   tiles skip the rescale; P is rounded to bf16 for the second MFMA; O accumulates in fp32
+//   and is rounded to bf16 once at the end.
 //
 // Memory path
 //   K and V tiles go HBM -> LDS directly (global_load_lds_dwordx4, 1 KB per wave
@@ -215,7 +216,8 @@ prefill_bf16_d128(AttnArgs a) {
     }
   }
 
-  auto compute_tile = [&](const bf16_t* kt, const bf16_t* vt, int j0, bool need_mask) __attribute__((always_inline)) {
+  auto compute_tile = [&](const bf16_t* kt, const bf16_t* vt, int j0, bool mask_hi, bool mask_lo)
+                          __attribute__((always_inline)) {
     f32x16 s0, s1;
 #pragma unroll
     for (int v = 0; v < 16; ++v) { s0[v] = 0.f; s1[v] = 0.f; }
@@ -238,16 +240,26 @@ prefill_bf16_d128(AttnArgs a) {
       s1 = mfma32x32x16(kf1[ks], qf[ks], s1);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (need_mask) {
-      asm volatile("");  // keeps this a branch: only tiles on a causal or window edge pay for it
-      // key offset e (from j0) of this lane's row is visible iff lo_lim < e <= hi_lim
-      const int hi_lim = my_pos - j0;
-      const int lo_lim = a.window > 0 ? my_pos - a.window - j0 : -(1 << 30);
+    // Index masks, each only on the tiles that need it: the causal limit (keys after a row's
+    // position) and the window edge (keys at or before position - W).
+    if (mask_hi) {
+      asm volatile("");  // keeps this a branch: only tiles on the diagonal pay for it
+      const int hi_lim = my_pos - j0;  // key offset e (from j0) is visible iff e <= hi_lim
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int e = 8 * (i >> 2) + 4 * hh + (i & 3);
-        s0[i] = (e <= hi_lim) & (e > lo_lim) ? s0[i] : SOC_NEG_INF;
-        s1[i] = (e + 32 <= hi_lim) & (e + 32 > lo_lim) ? s1[i] : SOC_NEG_INF;
+        s0[i] = e <= hi_lim ? s0[i] : SOC_NEG_INF;
+        s1[i] = e + 32 <= hi_lim ? s1[i] : SOC_NEG_INF;
+      }
+    }
+    if (mask_lo) {
+      asm volatile("");  // keeps this a branch: only tiles on a window edge pay for it
+      const int lo_lim = my_pos - a.window - j0;  // visible iff e > lo_lim
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int e = 8 * (i >> 2) + 4 * hh + (i & 3);
+        s0[i] = e > lo_lim ? s0[i] : SOC_NEG_INF;
+        s1[i] = e + 32 > lo_lim ? s1[i] : SOC_NEG_INF;
       }
     }
     float mx = fmaxf(s0[0], s1[0]);
@@ -302,9 +314,10 @@ prefill_bf16_d128(AttnArgs a) {
     const int j0 = t * KT;
     const bool skip = !wave_active || j0 > wpos_hi || (a.window > 0 && j0 + KT - 1 <= wpos_lo - a.window);
     if (!skip) {
-      // Only tiles that cross a row's causal limit or window edge apply the index mask.
-      const bool need_mask = (j0 + KT - 1 > wpos_lo) || (a.window > 0 && j0 <= wpos_hi - a.window);
-      compute_tile(kt, vt, j0, need_mask);
+      // Only tiles that cross a row's causal limit (or window edge) apply that index mask.
+      const bool mask_hi = j0 + KT - 1 > wpos_lo;
+      const bool mask_lo = a.window > 0 && j0 <= wpos_hi - a.window;
+      compute_tile(kt, vt, j0, mask_hi, mask_lo);
     }
     wait_vmem();
     __syncthreads();
