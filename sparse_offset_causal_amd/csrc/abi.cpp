@@ -384,6 +384,22 @@ int attn_ring_decode(const attn_shape_t* shape, const void* q, attn_strides_t q_
       if (h[b] < 0) return fail(ATTN_E_INVAL, "ATTN_DEBUG: n_seen[" + std::to_string(b) + "] is negative");
   }
 
+  if (shape->dtype == ATTN_BF16) {
+    // one kernel pass: the split holding each ring's slot substitutes and appends the new row
+    soc::AttnArgs a = make_args(shape, q, q_strides, k_ring, v_ring, ring_strides, o, o_strides, nullptr, 0, sink, scale);
+    a.part = static_cast<float*>(workspace);
+    a.nsplit = (int32_t)nsplit;
+    a.split = split;
+    a.ring_n = n_seen;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.new_sb = new_strides.b;
+    a.new_sh = new_strides.h;
+    hipError_t e = soc::launch_decode_bf16(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "attn_ring_decode split launch");
+    e = soc::launch_decode_merge(a, true, stream);
+    return finish(e, stream, "attn_ring_decode merge launch");
+  }
   int32_t* offs = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + part_bytes);
   soc::RingAppendArgs r{};
   r.k_new = k_new;
@@ -409,9 +425,9 @@ int attn_ring_decode(const attn_shape_t* shape, const void* q, attn_strides_t q_
   a.part = static_cast<float*>(workspace);
   a.nsplit = (int32_t)nsplit;
   a.split = split;
-  e = shape->dtype == ATTN_BF16 ? soc::launch_decode_bf16(a, stream) : soc::launch_decode_f32(a, stream);
+  e = soc::launch_decode_f32(a, stream);
   if (e != hipSuccess) return hip_fail(e, "attn_ring_decode split launch");
-  e = soc::launch_decode_merge(a, shape->dtype == ATTN_BF16, stream);
+  e = soc::launch_decode_merge(a, false, stream);
   return finish(e, stream, "attn_ring_decode merge launch");
 }
 

@@ -19,6 +19,11 @@
 // than 2^8).  The split's unnormalised partial (max, sum, O) is written in fp32.  The sink is
 // not applied here; the merge adds it exactly once per row.
 //
+// Ring mode (a W-slot ring per (sequence, KV head), n tokens written before the step): the
+// filled slots are 0 .. min(n, W - 1), and the split holding slot n % W stages the step's
+// new K/V row in LDS, puts it in place of the slot's old row (in the K registers and in the
+// V stage) when that block arrives, and writes it into the slot after its last read.
+//
 // Merge: per (b, h, r) row, M = max(max_s m_s, sink), L = sum_s l_s 2^(m_s - M) + 2^(sink - M),
 // o = sum_s o_s 2^(m_s - M) / L (all in the log2 domain), rounded once to the output type.
 
@@ -54,6 +59,7 @@ __device__ __forceinline__ void wait_blocks(int blocks_after) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+template <bool RING>
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
 decode_split_bf16_d128(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) bf16_t vlds[NST * VSTAGE];
@@ -64,11 +70,24 @@ decode_split_bf16_d128(AttnArgs a) {
   const int rem = blockIdx.x / a.nsplit;
   const int kvh = __builtin_amdgcn_readfirstlane(rem % a.Hkv);
   const int b = __builtin_amdgcn_readfirstlane(rem / a.Hkv);
-  const int off = __builtin_amdgcn_readfirstlane(a.cache_off ? a.cache_off[b] : a.tk - a.tq);
+  const int off = __builtin_amdgcn_readfirstlane(seq_cache_off(a, b));
   const int tkb = off + a.tq;
   const int nsb = (tkb + a.split - 1) / a.split;
   if (s >= nsb) return;  // the merge reads only splits below nsb
   const int ks0 = s * a.split, ks1 = min(ks0 + a.split, tkb);
+  // Ring mode: the split that holds slot ring_n[b] % tk attends over the step's new K/V row
+  // in place of the slot's old contents (staged in LDS) and writes the new row into the slot
+  // at its end.
+  __shared__ __attribute__((aligned(16))) bf16_t newrow[2][D];  // K then V of the step
+  const int slot = RING ? __builtin_amdgcn_readfirstlane(a.ring_n[b] % a.tk) : -1;
+  const bool own_slot = RING && slot >= ks0 && slot < ks1;
+  if (own_slot) {
+    const int64_t nrow = b * a.new_sb + kvh * a.new_sh;
+    if (lane < 16)
+      *(u32x4*)(&newrow[0][8 * lane]) = *(const u32x4*)((const bf16_t*)a.k_new + nrow + 8 * lane);
+    else if (lane < 32)
+      *(u32x4*)(&newrow[1][8 * (lane - 16)]) = *(const u32x4*)((const bf16_t*)a.v_new + nrow + 8 * (lane - 16));
+  }
   const int kv_lo = a.window > 0 ? max(0, off - a.window + 1) : 0;
   const int kbeg = max(ks0, kv_lo), kend = ks1;
   const int nblk = kbeg < kend ? (kend - kbeg + KB - 1) / KB : 0;
@@ -141,6 +160,14 @@ decode_split_bf16_d128(AttnArgs a) {
     wait_blocks(min(NST - 1, nblk - 1 - n));
     const bf16_t* vt = vlds + ST * VSTAGE;
     const int js = kbeg + n * KB;
+    if (RING && own_slot && slot >= js && slot < js + KB) {  // uniform: the ring slot being overwritten
+      const int rr = slot - js;
+      if (l32 == rr) {
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) kreg[ST][ks] = *(const bf16x8*)(&newrow[0][16 * ks + 8 * hh]);
+      }
+      if (lane < 16) *(u32x4*)(const_cast<bf16_t*>(vt) + v_off(rr, lane)) = *(const u32x4*)(&newrow[1][8 * lane]);
+    }
 
     f32x16 sacc;
 #pragma unroll
@@ -214,6 +241,13 @@ decode_split_bf16_d128(AttnArgs a) {
       pml[1] = L;
     }
   }
+  if (RING && own_slot) {  // the append: every load of the old slot has completed
+    const int64_t rrow = b * a.kv_sb + kvh * a.kv_sh + (int64_t)slot * a.kv_st;
+    if (lane < 16)
+      *(u32x4*)((bf16_t*)a.k + rrow + 8 * lane) = *(const u32x4*)(&newrow[0][8 * lane]);
+    else if (lane < 32)
+      *(u32x4*)((bf16_t*)a.v + rrow + 8 * (lane - 16)) = *(const u32x4*)(&newrow[1][8 * (lane - 16)]);
+  }
 }
 
 __device__ __forceinline__ float wave_max_f(float x) {
@@ -237,7 +271,7 @@ __global__ void __launch_bounds__(64) decode_merge(AttnArgs a) {
   const int r = (int)(rowid % a.tq);
   const int h = (int)((rowid / a.tq) % a.Hq);
   const int b = (int)(rowid / ((int64_t)a.tq * a.Hq));
-  const int off = a.cache_off ? a.cache_off[b] : a.tk - a.tq;
+  const int off = seq_cache_off(a, b);
   const int tkb = off + a.tq;
   const int nsb = __builtin_amdgcn_readfirstlane((tkb + a.split - 1) / a.split);
   const float* pml = a.part + decode_o_floats(a) + rowid * a.nsplit * 2;
@@ -296,7 +330,10 @@ __global__ void __launch_bounds__(64) decode_merge(AttnArgs a) {
 hipError_t launch_decode_bf16(const AttnArgs& a, hipStream_t s) {
   const int64_t grid = (int64_t)a.B * a.Hkv * a.nsplit;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(decode_split_bf16_d128, dim3((unsigned)grid), dim3(64), 0, s, a);
+  if (a.ring_n)
+    hipLaunchKernelGGL(decode_split_bf16_d128<true>, dim3((unsigned)grid), dim3(64), 0, s, a);
+  else
+    hipLaunchKernelGGL(decode_split_bf16_d128<false>, dim3((unsigned)grid), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 

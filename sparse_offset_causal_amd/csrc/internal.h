@@ -30,7 +30,21 @@ struct AttnArgs {
   float* part;     // workspace: partial sums, [B*Hq*tq][nsplit][d] floats, then [..][nsplit][2]
   int32_t nsplit;  // splits per sequence (capacity)
   int32_t split;   // keys per split
+  // ring-buffer decode (bf16): the cache is a tk-slot ring per (sequence, KV head), ring_n[b]
+  // tokens written before this step; the step's K/V rows (k_new, v_new) go to slot
+  // ring_n[b] % tk, and the step attends over the min(ring_n[b] + 1, tk) filled slots.
+  const int32_t* ring_n;  // device [B] or null (no ring)
+  const void* k_new;
+  const void* v_new;
+  int64_t new_sb, new_sh;
 };
+
+// Cache offset of sequence b: the ring's filled slots minus one, the caller's offset, or
+// tk - tq.
+__device__ inline int seq_cache_off(const AttnArgs& a, int b) {
+  if (a.ring_n) return min(a.ring_n[b], a.tk - 1);
+  return a.cache_off ? a.cache_off[b] : a.tk - a.tq;
+}
 
 // Decode workspace layout helpers (floats).
 __host__ __device__ inline size_t decode_rows(const AttnArgs& a) { return (size_t)a.B * a.Hq * a.tq; }

@@ -3,9 +3,10 @@
 // A layer that attends only to the last W tokens keeps W slots per KV head; token number n
 // goes into slot n mod W, overwriting the oldest entry, and attention runs over the filled
 // slots in any order (sotaaz.com/post/attention-in-code, section 2, the ring-buffer cache).
-// This kernel writes one step's K and V rows into their slot and, per sequence, the offset
-// that makes the split-KV decode read exactly the filled slots: with min(n + 1, W) slots
-// filled, a one-row query at cache offset min(n, W - 1) sees slots 0 .. min(n, W - 1).
+// This kernel (the fp32 path; the bf16 split-KV decode substitutes and appends the new row
+// itself) writes one step's K and V rows into their slot and, per sequence, the offset that
+// makes the split-KV decode read exactly the filled slots: with min(n + 1, W) slots filled,
+// a one-row query at cache offset min(n, W - 1) sees slots 0 .. min(n, W - 1).
 //
 // One workgroup of 64 threads per (sequence, KV head); each thread copies one 16-byte
 // chunk of the K row or of the V row (a row is at most 512 bytes: 32 chunks).
