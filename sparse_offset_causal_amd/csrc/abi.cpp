@@ -332,6 +332,9 @@ int attn_decode(const attn_shape_t* shape, const void* q, attn_strides_t q_strid
   a.part = static_cast<float*>(workspace);
   a.nsplit = (int32_t)nsplit;
   a.split = split;
+  // longest-first order once the splits take more than one round of the chip (about six
+  // single-wave split workgroups fit on a CU)
+  a.lpt = (int64_t)shape->batch * shape->n_kv * nsplit > 6 * (int64_t)device_cus();
   hipError_t e = shape->dtype == ATTN_BF16 ? soc::launch_decode_bf16(a, stream) : soc::launch_decode_f32(a, stream);
   if (e != hipSuccess) return hip_fail(e, "attn_decode split launch");
   e = soc::launch_decode_merge(a, shape->dtype == ATTN_BF16, stream);

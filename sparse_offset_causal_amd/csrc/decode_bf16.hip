@@ -19,6 +19,14 @@
 // than 2^8).  The split's unnormalised partial (max, sum, O) is written in fp32.  The sink is
 // not applied here; the merge adds it exactly once per row.
 //
+// Work order: when the grid takes several rounds of the chip, workgroup i does not take the
+// i-th (sequence, KV head, split) in grid order but the i-th in longest-first order: every
+// full split, then the partial splits by block count (largest first), then the empty splits
+// below a window; sequence, split and KV head break ties.  Each workgroup finds its item from
+// the sequence lengths with wave prefix sums and a 64-bucket histogram of the partial sizes.
+// Without it the splits of the last sequences in grid order start last and the chip idles
+// while they finish.
+//
 // Ring mode (a W-slot ring per (sequence, KV head), n tokens written before the step): the
 // filled slots are 0 .. min(n, W - 1), and the split holding slot n % W stages the step's
 // new K/V row in LDS, puts it in place of the slot's old row (in the K registers and in the
@@ -59,6 +67,113 @@ __device__ __forceinline__ void wait_blocks(int blocks_after) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+__device__ __forceinline__ int wave_incl_prefix(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// The (sequence, KV head, split) of workgroup `item` in longest-first order (see the header);
+// false when the item is past the last split of the call.  hist: 64 ints of LDS.  One wave.
+__device__ bool lpt_item(const AttnArgs& a, int item, int* hist, int& b_out, int& kvh_out, int& s_out) {
+  const int lane = threadIdx.x & 63;
+  const int fb = (a.split + KB - 1) / KB;  // blocks of a full split
+  const int unit = item / a.Hkv;
+  kvh_out = item - unit * a.Hkv;
+  // Splits of sequence bb: s < s_lo are empty (below the window), s_lo is the first with keys,
+  // nsb - 1 the last; the full ones are sf0 .. sf0 + nfull - 1; p1 / p2 are the block counts of
+  // the first / last split when it is partial (else 0).
+  auto info = [&](int bb, int& s_lo, int& nsb, int& sf0, int& nfull, int& p1, int& p2) __attribute__((always_inline)) {
+    s_lo = nsb = sf0 = nfull = p1 = p2 = 0;
+    if (bb >= a.B) return;
+    const int off = seq_cache_off(a, bb);
+    const int tkb = off + a.tq;
+    const int kv_lo = a.window > 0 ? max(0, off - a.window + 1) : 0;
+    nsb = (tkb + a.split - 1) / a.split;
+    s_lo = kv_lo / a.split;
+    const int bf = (min((s_lo + 1) * a.split, tkb) - kv_lo + KB - 1) / KB;
+    const bool has_last = nsb - 1 > s_lo;
+    const int bl = has_last ? (tkb - (nsb - 1) * a.split + KB - 1) / KB : 0;
+    sf0 = bf == fb ? s_lo : s_lo + 1;
+    const int sf1 = has_last ? (bl == fb ? nsb - 1 : nsb - 2) : (bf == fb ? s_lo : s_lo - 1);
+    nfull = max(0, sf1 - sf0 + 1);
+    p1 = bf < fb ? bf : 0;
+    p2 = has_last && bl < fb ? bl : 0;
+  };
+  auto cls = [&](int blocks) __attribute__((always_inline)) { return (blocks * 64 - 1) / fb; };  // 0..63
+  int s_lo, nsb, sf0, nfull, p1, p2;
+  // full splits, in (sequence, split) order
+  int base = 0;
+  for (int c0 = 0; c0 < a.B; c0 += 64) {
+    info(c0 + lane, s_lo, nsb, sf0, nfull, p1, p2);
+    const int incl = base + wave_incl_prefix(nfull);
+    const unsigned long long own = __ballot(nfull > 0 && unit < incl && unit >= incl - nfull);
+    if (own) {
+      const int L = __ffsll(own) - 1;
+      b_out = c0 + L;
+      s_out = __builtin_amdgcn_readlane(sf0 + unit - (incl - nfull), L);
+      return true;
+    }
+    base = __builtin_amdgcn_readlane(incl, 63);
+  }
+  int u = unit - base;
+  // partial splits, largest block count first: histogram of their size classes
+  hist[lane] = 0;
+  __syncthreads();
+  for (int c0 = 0; c0 < a.B; c0 += 64) {
+    info(c0 + lane, s_lo, nsb, sf0, nfull, p1, p2);
+    if (p1) atomicAdd(&hist[cls(p1)], 1);
+    if (p2) atomicAdd(&hist[cls(p2)], 1);
+  }
+  __syncthreads();
+  const int hc = hist[63 - lane];  // lane r: class 63 - r, so the prefix runs largest first
+  const int hincl = wave_incl_prefix(hc);
+  const int ptotal = __builtin_amdgcn_readlane(hincl, 63);
+  if (u < ptotal) {
+    const unsigned long long ownc = __ballot(hc > 0 && u < hincl && u >= hincl - hc);
+    const int r = __ffsll(ownc) - 1;
+    const int csel = 63 - r;
+    const int m = u - __builtin_amdgcn_readlane(hincl - hc, r);  // rank within the class
+    base = 0;
+    for (int c0 = 0; c0 < a.B; c0 += 64) {
+      info(c0 + lane, s_lo, nsb, sf0, nfull, p1, p2);
+      const int c1 = p1 && cls(p1) == csel, c2 = p2 && cls(p2) == csel;
+      const int cnt = c1 + c2;
+      const int incl = base + wave_incl_prefix(cnt);
+      const unsigned long long own = __ballot(cnt > 0 && m < incl && m >= incl - cnt);
+      if (own) {
+        const int L = __ffsll(own) - 1;
+        const int k = m - (incl - cnt);  // 0: this sequence's first such split, 1: its second
+        b_out = c0 + L;
+        s_out = __builtin_amdgcn_readlane(c1 && k == 0 ? s_lo : nsb - 1, L);
+        return true;
+      }
+      base = __builtin_amdgcn_readlane(incl, 63);
+    }
+    return false;  // not reached: the histogram counted this split
+  }
+  u -= ptotal;
+  // empty splits below a window, in (sequence, split) order
+  base = 0;
+  for (int c0 = 0; c0 < a.B; c0 += 64) {
+    info(c0 + lane, s_lo, nsb, sf0, nfull, p1, p2);
+    const int incl = base + wave_incl_prefix(s_lo);
+    const unsigned long long own = __ballot(s_lo > 0 && u < incl && u >= incl - s_lo);
+    if (own) {
+      const int L = __ffsll(own) - 1;
+      b_out = c0 + L;
+      s_out = __builtin_amdgcn_readlane(u - (incl - s_lo), L);
+      return true;
+    }
+    base = __builtin_amdgcn_readlane(incl, 63);
+  }
+  return false;
+}
+
 template <bool RING>
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
 decode_split_bf16_d128(AttnArgs a) {
@@ -66,10 +181,26 @@ decode_split_bf16_d128(AttnArgs a) {
 
   const int lane = threadIdx.x;
   const int l32 = lane & 31, hh = lane >> 5;
-  const int s = __builtin_amdgcn_readfirstlane(blockIdx.x % a.nsplit);
-  const int rem = blockIdx.x / a.nsplit;
-  const int kvh = __builtin_amdgcn_readfirstlane(rem % a.Hkv);
-  const int b = __builtin_amdgcn_readfirstlane(rem / a.Hkv);
+  int s_i, kvh_i, b_i;
+  if constexpr (!RING) {
+    __shared__ int lpt_hist[64];
+    if (a.lpt) {
+      if (!lpt_item(a, blockIdx.x, lpt_hist, b_i, kvh_i, s_i)) return;
+    } else {
+      s_i = blockIdx.x % a.nsplit;
+      const int rem = blockIdx.x / a.nsplit;
+      kvh_i = rem % a.Hkv;
+      b_i = rem / a.Hkv;
+    }
+  } else {
+    s_i = blockIdx.x % a.nsplit;
+    const int rem = blockIdx.x / a.nsplit;
+    kvh_i = rem % a.Hkv;
+    b_i = rem / a.Hkv;
+  }
+  const int s = __builtin_amdgcn_readfirstlane(s_i);
+  const int kvh = __builtin_amdgcn_readfirstlane(kvh_i);
+  const int b = __builtin_amdgcn_readfirstlane(b_i);
   const int off = __builtin_amdgcn_readfirstlane(seq_cache_off(a, b));
   const int tkb = off + a.tq;
   const int nsb = (tkb + a.split - 1) / a.split;

@@ -30,6 +30,7 @@ struct AttnArgs {
   float* part;     // workspace: partial sums, [B*Hq*tq][nsplit][d] floats, then [..][nsplit][2]
   int32_t nsplit;  // splits per sequence (capacity)
   int32_t split;   // keys per split
+  int32_t lpt;     // bf16 decode: workgroups take the splits longest first (grids of several rounds)
   // ring-buffer decode (bf16): the cache is a tk-slot ring per (sequence, KV head), ring_n[b]
   // tokens written before this step; the step's K/V rows (k_new, v_new) go to slot
   // ring_n[b] % tk, and the step attends over the min(ring_n[b] + 1, tk) filled slots.

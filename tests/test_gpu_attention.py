@@ -194,6 +194,26 @@ def test_bf16_decode_window_and_mqa():
     assert max_abs(o, oracle_of(w)) <= BF16_TOL
 
 
+@pytest.mark.parametrize("tq,window,split", [(1, 0, 128), (1, 700, 128), (4, 1000, 96), (2, 0, 300)])
+def test_bf16_decode_longest_first_order(tq, window, split):
+    """Grids of several rounds of the chip take the splits longest first (full, then partial by
+    size, then the empty ones below a window); every split must still be computed exactly once.
+    70 sequences (two 64-lane chunks of the work-order prefix sums), lengths on split edges."""
+    announce(f"bf16 decode longest-first tq={tq} window={window} split={split}")
+    B, Hq, Hkv = 70, 8, 2
+    g = torch.Generator().manual_seed(40 + tq)
+    lengths = torch.randint(1, 3000, (B,), generator=g).tolist()
+    lengths[:8] = [1, split - 1, split, split + 1, 2 * split, 2999, 31, 33]
+    cap = 3000 + tq
+    nsplit = -(-cap // split)
+    assert B * Hkv * nsplit > 6 * torch.cuda.get_device_properties(0).multi_processor_count
+    w = synth.attention_inputs(B, Hq, Hkv, tq, cap, 128, torch.bfloat16, seed=50 + tq, with_sink=True,
+                               window=window, cache_off=lengths)
+    o = attn_decode(dev(w.q), dev(w.k), dev(w.v), cache_off=dev(w.cache_off), window=window, sink=dev(w.sink),
+                    split_tokens=split)
+    assert max_abs(o, oracle_of(w)) <= BF16_TOL
+
+
 def test_bf16_decode_rejects_too_many_rows():
     w = synth.attention_inputs(1, 32, 4, 8, 64, 128, torch.bfloat16, seed=1)
     with pytest.raises(AttnError, match="32 query rows"):
