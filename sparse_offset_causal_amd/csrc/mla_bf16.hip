@@ -319,29 +319,47 @@ __global__ void __launch_bounds__(256) mla_merge_kernel(MlaArgs a) {
   }
   __syncthreads();
   const int d = half * 256 + threadIdx.x;
-  float acc = 0.f;
-  for (int k = 0; k < nsb; ++k) acc = fmaf(wgt[k], a.part_o[(p0 + k) * MR + d], acc);
-  a.o_lat[(int64_t)row * MR + d] = acc * inv_l;
+  // eight splits per step with independent accumulators, so eight loads are in flight
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  int k = 0;
+  for (; k + 8 <= nsb; k += 8) {
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = a.part_o[(p0 + k + e) * MR + d];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = fmaf(wgt[k + e], x[e], acc[e]);
+  }
+  for (; k < nsb; ++k) acc[k & 7] = fmaf(wgt[k], a.part_o[(p0 + k) * MR + d], acc[k & 7]);
+  const float sum = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+  a.o_lat[(int64_t)row * MR + d] = sum * inv_l;
 }
 
 // o[row, 32q + j] = sum_r o_lat[row, r] w_uv[h, r, 32q + j] for 16 rows (b, t) of head h
 // (grid: H x row groups x 4 quarters of the output width).
 __global__ void __launch_bounds__(256) mla_expand_kernel(MlaArgs a) {
-  __shared__ float ol[16][MR];
+  __shared__ __attribute__((aligned(16))) float ol[16][MR];
   __shared__ __attribute__((aligned(16))) bf16_t ws[MR][32];  // w_uv[h][:, 32 q4 .. 32 q4 + 31]
   const int q4 = blockIdx.x & 3;
   const int hg = blockIdx.x >> 2;
   const int h = hg % a.H, grp = hg / a.H;
   const int nrow = a.B * a.tq;
   const int R = a.H * a.tq;
-  for (int i = threadIdx.x; i < 16 * MR; i += 256) {
-    const int r = i / MR, d = i % MR, idx = grp * 16 + r;
-    float v = 0.f;
-    if (idx < nrow) {
-      const int b = idx / a.tq, t = idx % a.tq;
-      v = a.o_lat[((int64_t)b * R + h * a.tq + t) * MR + d];
+  {  // the 16 latent rows in 16-byte pieces, all loads in flight at once: rows past the end
+     // load the last row (no branch around the loads) and are stored as 0
+    f32x4 v[16 * MR / 4 / 256];
+#pragma unroll
+    for (int k = 0; k < 16 * MR / 4 / 256; ++k) {
+      const int i = threadIdx.x + 256 * k, r = i / (MR / 4), c = i % (MR / 4);
+      const int idx = min(grp * 16 + r, nrow - 1);
+      const int b = idx / a.tq, t = idx - b * a.tq;
+      v[k] = *(const f32x4*)(a.o_lat + ((int64_t)b * R + h * a.tq + t) * MR + 4 * c);
     }
-    ol[r][d] = v;
+#pragma unroll
+    for (int k = 0; k < 16 * MR / 4 / 256; ++k) {
+      const int i = threadIdx.x + 256 * k, r = i / (MR / 4), c = i % (MR / 4);
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      *(f32x4*)&ol[r][4 * c] = grp * 16 + r < nrow ? v[k] : z;
+    }
   }
   {  // the 512 x 32 weight slice in 16-byte pieces, all loads in flight at once
     const bf16_t* wsrc = (const bf16_t*)a.w_uv + (int64_t)h * MR * MDV + 32 * q4;
