@@ -18,8 +18,12 @@ counted).  Decode bytes = K and V rows each sequence must read (2 * n_kv * Tk_b 
 plus q and o.  Inputs are resident in HBM before timing starts.
 
 Timing: ``warmup`` untimed steps, then exactly ``steps`` steps between two device
-synchronisations; per-launch durations come from HIP events recorded on the stream the
-kernels run on.  ``cpu_baseline`` times the float64 oracle on the host on a bounded sample.
+synchronisations, with one pair of HIP events on the stream the kernels run on bracketing
+the timed steps (GPU time per step = their elapsed time / steps).  Per-call event timings
+(an event pair around each call, which adds a few microseconds of queue serialisation per
+call) are taken on a few extra calls after the timed region and reported as
+``call_ms_median`` / ``call_ms_min``.  ``cpu_baseline`` times the float64 oracle on the host
+on a bounded sample.
 """
 from __future__ import annotations
 
@@ -70,7 +74,10 @@ def block_pairs(bs: int, qb: int, kb: int) -> int:
 
 # ------------------------------------------------------------------ timing
 class Timer:
-    """Times `steps` calls of fn between synchronisations, with per-call HIP events."""
+    """Times `steps` calls of fn between synchronisations.  The timed region holds only the
+    calls: the wall clock and one pair of HIP events on the launch stream bracket it (the
+    events give the mean GPU time per step).  Per-call event timings, which put an event pair
+    around every call and so perturb short steps, are taken afterwards on a few extra calls."""
 
     def __init__(self, fn, steps, warmup):
         self.fn, self.steps, self.warmup = fn, steps, warmup
@@ -80,17 +87,25 @@ class Timer:
             self.fn()
         torch.cuda.synchronize()
         stream = torch.cuda.current_stream()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(self.steps)]
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
+        start.record(stream)
+        for _ in range(self.steps):
+            self.fn()
+        end.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        gpu_ms = start.elapsed_time(end) / self.steps
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(min(self.steps, 10))]
         for s, e in ev:
             s.record(stream)
             self.fn()
             e.record(stream)
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
         per = [s.elapsed_time(e) for s, e in ev]  # ms
-        return dict(wall_s=wall, ms_per_step=wall * 1e3 / self.steps, launch_ms_mean=float(np.mean(per)),
-                    launch_ms_median=float(np.median(per)), launch_ms_min=float(np.min(per)))
+        return dict(wall_s=wall, ms_per_step=wall * 1e3 / self.steps, gpu_ms_per_step=gpu_ms,
+                    call_ms_median=float(np.median(per)), call_ms_min=float(np.min(per)))
 
 
 def to_dev(w):
@@ -107,7 +122,7 @@ def bench_causal_prefill(steps, warmup, T=8192):
     r = Timer(fn, steps, warmup).run()
     flops = prefill_flops(32, 128, allowed_pairs(T, T, 0))
     r.update(workload=w.name, flops_per_step=flops, value=flops / (r["ms_per_step"] * 1e-3) / 1e12,
-             kernel_tflops=flops / (r["launch_ms_mean"] * 1e-3) / 1e12, unit="TFLOP/s")
+             kernel_tflops=flops / (r["gpu_ms_per_step"] * 1e-3) / 1e12, unit="TFLOP/s")
     return r, w
 
 
@@ -119,7 +134,7 @@ def bench_window_sink(steps, warmup, T=32768, W=1024):
     r = Timer(fn, steps, warmup).run()
     flops = prefill_flops(32, 128, allowed_pairs(T, T, W))
     r.update(workload=w.name, flops_per_step=flops, value=flops / (r["ms_per_step"] * 1e-3) / 1e12,
-             kernel_tflops=flops / (r["launch_ms_mean"] * 1e-3) / 1e12, unit="TFLOP/s")
+             kernel_tflops=flops / (r["gpu_ms_per_step"] * 1e-3) / 1e12, unit="TFLOP/s")
     return r
 
 
@@ -139,7 +154,7 @@ def bench_decode_and_chunk(steps, warmup, B=64):
     qo_bytes = float(2 * B * Hq * d * 2)
     nbytes = kv_bytes + qo_bytes
     rd.update(workload=f"decode_bf16_B{B}_cache1024-32768_{Hq}q{Hkv}kv_d{d}", bytes_per_step=nbytes,
-              value=nbytes / (rd["ms_per_step"] * 1e-3) / 1e9, kernel_GBps=nbytes / (rd["launch_ms_mean"] * 1e-3) / 1e9,
+              value=nbytes / (rd["ms_per_step"] * 1e-3) / 1e9, kernel_GBps=nbytes / (rd["gpu_ms_per_step"] * 1e-3) / 1e9,
               unit="GB/s", mean_cache_len=float(L.mean()))
     qc = c.q_chunk.to("cuda")
     oc = torch.empty_like(qc)
@@ -148,7 +163,7 @@ def bench_decode_and_chunk(steps, warmup, B=64):
     pairs = float(sum(allowed_pairs(c.chunk, int(l) + c.chunk, 0) for l in L))
     flops = prefill_flops(Hq, d, pairs)
     rc.update(workload=f"chunk512_bf16_B{B}_cache1024-32768_{Hq}q{Hkv}kv_d{d}", flops_per_step=flops,
-              value=flops / (rc["ms_per_step"] * 1e-3) / 1e12, kernel_tflops=flops / (rc["launch_ms_mean"] * 1e-3) / 1e12,
+              value=flops / (rc["ms_per_step"] * 1e-3) / 1e12, kernel_tflops=flops / (rc["gpu_ms_per_step"] * 1e-3) / 1e12,
               unit="TFLOP/s")
     del k, v
     return rd, rc
@@ -169,7 +184,7 @@ def bench_ring_decode(steps, warmup, B=64, W=1024):
     other = float(2 * B * Hq * d * 2 + 2 * 2 * B * Hkv * d * 2)  # q, o; new K/V read and written
     nbytes = kv_bytes + other
     r.update(workload=f"ring_decode_bf16_B{B}_W{W}_{Hq}q{Hkv}kv_d{d}", bytes_per_step=nbytes,
-             value=nbytes / (r["ms_per_step"] * 1e-3) / 1e9, kernel_GBps=nbytes / (r["launch_ms_mean"] * 1e-3) / 1e9,
+             value=nbytes / (r["ms_per_step"] * 1e-3) / 1e9, kernel_GBps=nbytes / (r["gpu_ms_per_step"] * 1e-3) / 1e9,
              unit="GB/s")
     return r
 
@@ -189,7 +204,7 @@ def bench_mla_decode(steps, warmup, B=64, H=16):
     other = float(B * H * (128 + 64 + 128) * 2 + 2 * H * 512 * 128 * 2)  # q, o, w_uk, w_uv
     nbytes = lat_bytes + other
     r.update(workload=f"mla_decode_bf16_B{B}_H{H}_cache1024-32768_r512_rope64", bytes_per_step=nbytes,
-             value=nbytes / (r["ms_per_step"] * 1e-3) / 1e9, kernel_GBps=nbytes / (r["launch_ms_mean"] * 1e-3) / 1e9,
+             value=nbytes / (r["ms_per_step"] * 1e-3) / 1e9, kernel_GBps=nbytes / (r["gpu_ms_per_step"] * 1e-3) / 1e9,
              unit="GB/s")
     del ck, kr
     return r
@@ -213,7 +228,7 @@ def bench_dsa_decode(steps, warmup, B=64, topk=2048):
     nbytes = idx_bytes + kv_bytes + other
     r.update(workload=f"dsa_decode_bf16_B{B}_cache1024-32768_{Hq}q{Hkv}kv_d{d}_idx{Hi}x128_top{topk}",
              bytes_per_step=nbytes, value=nbytes / (r["ms_per_step"] * 1e-3) / 1e9,
-             kernel_GBps=nbytes / (r["launch_ms_mean"] * 1e-3) / 1e9, unit="GB/s")
+             kernel_GBps=nbytes / (r["gpu_ms_per_step"] * 1e-3) / 1e9, unit="GB/s")
     del k, v
     return r
 
@@ -236,7 +251,7 @@ def bench_block_sparse(steps, warmup, T=65536, BS=128):
     adm = 32 * nb * (nb + 1) // 2
     sel_bytes = float(q.numel() * 2 + k.numel() * 2)
     rp.update(workload=f"block_sparse_prefill_bf16_T{T}_BS{BS}_32q8kv_d128", flops_per_step=flops,
-              value=flops / (rp["ms_per_step"] * 1e-3) / 1e12, kernel_tflops=flops / (rp["launch_ms_mean"] * 1e-3) / 1e12,
+              value=flops / (rp["ms_per_step"] * 1e-3) / 1e12, kernel_tflops=flops / (rp["gpu_ms_per_step"] * 1e-3) / 1e12,
               unit="TFLOP/s", kept_fraction=total / adm)
     rs.update(workload=f"block_select_fp64_T{T}_BS{BS}_32q8kv_d128", bytes_per_step=sel_bytes,
               value=sel_bytes / (rs["ms_per_step"] * 1e-3) / 1e9, unit="GB/s (q+k read)")
@@ -322,8 +337,8 @@ def main():
         src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
         r = Timer(lambda: dst.copy_(src), args.steps, args.warmup).run()
-        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms": r["launch_ms_mean"],
-                          "GBps_read_plus_write": 2 * n / (r["launch_ms_mean"] * 1e-3) / 1e9}), flush=True)
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms": r["gpu_ms_per_step"],
+                          "GBps_read_plus_write": 2 * n / (r["gpu_ms_per_step"] * 1e-3) / 1e9}), flush=True)
         return
 
     also = {}
@@ -371,10 +386,10 @@ def main():
                 break
     roof_bound = "hbm" if head["unit"] == "GB/s" else "mfma"
     if roof_bound == "mfma":
-        achieved = head["flops_per_step"] / (head["launch_ms_mean"] * 1e-3) / 1e12
+        achieved = head["flops_per_step"] / (head["gpu_ms_per_step"] * 1e-3) / 1e12
         peak, unit = PEAK_BF16_TFLOPS, "TFLOP/s"
     else:
-        achieved = head["bytes_per_step"] / (head["launch_ms_mean"] * 1e-3) / 1e9
+        achieved = head["bytes_per_step"] / (head["gpu_ms_per_step"] * 1e-3) / 1e9
         peak, unit = PEAK_HBM_GBPS, "GB/s"
     measured = load_traffic(args.traffic)
     traffic = measured.get(head["workload"])
