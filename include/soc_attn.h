@@ -157,9 +157,12 @@ size_t attn_ring_decode_workspace_bytes(const attn_shape_t* shape, int32_t split
  *  workspace  at least attn_ring_decode_workspace_bytes(shape, split_tokens) bytes.
  * bf16: the split-KV decode of attn_decode runs over the ring itself; the split that holds
  * slot n_seen[b] % W attends over the new row in place of the slot's old contents and writes
- * the new row into the slot when it has finished reading (one kernel and the merge).  fp32:
- * a small append kernel writes the rows first, then the split-KV decode and merge run.  Same
- * dtype and head_dim rules as attn_decode; bf16 needs n_heads / n_kv <= 32.
+ * the new row into the slot when it has finished reading.  With at most two splits per ring
+ * (the default for W up to twice the split size) both splits of a (sequence, KV head) run in
+ * one workgroup and merge there: one kernel, the workspace unused.  With more splits the
+ * split kernel writes partials to the workspace and the merge kernel follows.  fp32: a small
+ * append kernel writes the rows first, then the split-KV decode and merge run.  Same dtype
+ * and head_dim rules as attn_decode; bf16 needs n_heads / n_kv <= 32.
  */
 int attn_ring_decode(const attn_shape_t* shape, const void* q, attn_strides_t q_strides, const void* k_new,
                      const void* v_new, attn_strides_t new_strides, void* k_ring, void* v_ring,

@@ -398,7 +398,9 @@ int attn_ring_decode(const attn_shape_t* shape, const void* q, attn_strides_t q_
     a.v_new = v_new;
     a.new_sb = new_strides.b;
     a.new_sh = new_strides.h;
+    a.fused = nsplit <= 2;  // both splits of a ring in one workgroup, merged there
     hipError_t e = soc::launch_decode_bf16(a, stream);
+    if (a.fused) return finish(e, stream, "attn_ring_decode launch");
     if (e != hipSuccess) return hip_fail(e, "attn_ring_decode split launch");
     e = soc::launch_decode_merge(a, true, stream);
     return finish(e, stream, "attn_ring_decode merge launch");

@@ -174,15 +174,22 @@ __device__ bool lpt_item(const AttnArgs& a, int item, int* hist, int& b_out, int
   return false;
 }
 
-template <bool RING>
-__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
+template <bool RING, bool FUSED>
+__global__ void __launch_bounds__(FUSED ? 128 : 64) __attribute__((amdgpu_waves_per_eu(2)))
 decode_split_bf16_d128(AttnArgs a) {
-  __shared__ __attribute__((aligned(1024))) bf16_t vlds[NST * VSTAGE];
+  constexpr int NW = FUSED ? 2 : 1;  // waves (splits) per workgroup
+  __shared__ __attribute__((aligned(1024))) bf16_t vlds[NW * NST * VSTAGE];
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = FUSED ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
   const int l32 = lane & 31, hh = lane >> 5;
+  bf16_t* const vbase = vlds + wave * (NST * VSTAGE);  // this wave's V stages
   int s_i, kvh_i, b_i;
-  if constexpr (!RING) {
+  if constexpr (FUSED) {
+    s_i = wave;
+    kvh_i = blockIdx.x % a.Hkv;
+    b_i = blockIdx.x / a.Hkv;
+  } else if constexpr (!RING) {
     __shared__ int lpt_hist[64];
     if (a.lpt) {
       if (!lpt_item(a, blockIdx.x, lpt_hist, b_i, kvh_i, s_i)) return;
@@ -204,12 +211,13 @@ decode_split_bf16_d128(AttnArgs a) {
   const int off = __builtin_amdgcn_readfirstlane(seq_cache_off(a, b));
   const int tkb = off + a.tq;
   const int nsb = (tkb + a.split - 1) / a.split;
-  if (s >= nsb) return;  // the merge reads only splits below nsb
+  if (!FUSED && s >= nsb) return;  // the merge reads only splits below nsb
   const int ks0 = s * a.split, ks1 = min(ks0 + a.split, tkb);
   // Ring mode: the split that holds slot ring_n[b] % tk attends over the step's new K/V row
   // in place of the slot's old contents (staged in LDS) and writes the new row into the slot
   // at its end.
-  __shared__ __attribute__((aligned(16))) bf16_t newrow[2][D];  // K then V of the step
+  __shared__ __attribute__((aligned(16))) bf16_t newrow_w[NW][2][D];  // K then V of the step
+  bf16_t (&newrow)[2][D] = newrow_w[wave];
   const int slot = RING ? __builtin_amdgcn_readfirstlane(a.ring_n[b] % a.tk) : -1;
   const bool own_slot = RING && slot >= ks0 && slot < ks1;
   if (own_slot) {
@@ -244,7 +252,7 @@ decode_split_bf16_d128(AttnArgs a) {
       kreg[ST][ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(krs, k_lane + ks * 32, blk_off, 0));
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void_ptr)(vlds + ST * VSTAGE + i * 512), 16, v_lane,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void_ptr)(vbase + ST * VSTAGE + i * 512), 16, v_lane,
                                                blk_off + 4 * i * row_bytes, 0, 0);
   };
 
@@ -289,7 +297,7 @@ decode_split_bf16_d128(AttnArgs a) {
     constexpr int ST = decltype(stage_tag)::value;
     if (n + NST - 1 < nblk) issue(n + NST - 1, std::integral_constant<int, (ST + NST - 1) % NST>{});
     wait_blocks(min(NST - 1, nblk - 1 - n));
-    const bf16_t* vt = vlds + ST * VSTAGE;
+    const bf16_t* vt = vbase + ST * VSTAGE;
     const int js = kbeg + n * KB;
     if (RING && own_slot && slot >= js && slot < js + KB) {  // uniform: the ring slot being overwritten
       const int rr = slot - js;
@@ -354,7 +362,44 @@ decode_split_bf16_d128(AttnArgs a) {
   }
 
   const float L = pair_sum(l_run);
-  if (row_ok) {
+  if constexpr (FUSED) {
+    // Merge of the workgroup's two splits: the (max, sum) pairs through LDS, each wave scales
+    // its O by 2^(m - M) / L_total (the sink counted once), wave 1 hands its share to wave 0
+    // through its own V stages (idle once its loop is done), and wave 0 writes the output.
+    __shared__ float mlx[2][32][2];
+    if (hh == 0) {
+      mlx[wave][l32][0] = m_run;
+      mlx[wave][l32][1] = L;
+    }
+    __syncthreads();
+    const float m0 = mlx[0][l32][0], m1 = mlx[1][l32][0];
+    const float sink_l2 = a.sink && row_ok ? a.sink[h] * kLog2e : SOC_NEG_INF;
+    const float M = fmaxf(fmaxf(m0, m1), sink_l2);
+    const float Mu = M == SOC_NEG_INF ? 0.f : M;
+    const float Lt = mlx[0][l32][1] * fast_exp2(m0 - Mu) + mlx[1][l32][1] * fast_exp2(m1 - Mu) + fast_exp2(sink_l2 - Mu);
+    const float wgt = Lt > 0.f ? fast_exp2(m_run - Mu) / Lt : 0.f;
+    float* xo = reinterpret_cast<float*>(vlds + NST * VSTAGE);  // wave 1's stages: 64 floats per lane
+    if (wave == 1) {
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) xo[(tb * 16 + v) * 64 + lane] = oacc[tb][v] * wgt;
+    }
+    __syncthreads();
+    if (wave == 0 && row_ok) {
+      bf16_t* orow = (bf16_t*)a.o + b * a.o_sb + h * a.o_sh + (int64_t)r * a.o_st;
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          bf16x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            w[e] = (bf16_t)fmaf(oacc[tb][4 * g4 + e], wgt, xo[(tb * 16 + 4 * g4 + e) * 64 + lane]);
+          *(bf16x4*)(orow + tb * 32 + 8 * g4 + 4 * hh) = w;
+        }
+    }
+  } else if (row_ok) {
     const int64_t rowid = ((int64_t)b * a.Hq + h) * a.tq + r;
     float* po = a.part + (rowid * a.nsplit + s) * D;
 #pragma unroll
@@ -459,12 +504,18 @@ __global__ void __launch_bounds__(64) decode_merge(AttnArgs a) {
 }  // namespace
 
 hipError_t launch_decode_bf16(const AttnArgs& a, hipStream_t s) {
+  if (a.fused) {  // ring decode, at most two splits: both in one workgroup, merged in place
+    const int64_t grid = (int64_t)a.B * a.Hkv;
+    if (grid == 0) return hipSuccess;
+    hipLaunchKernelGGL((decode_split_bf16_d128<true, true>), dim3((unsigned)grid), dim3(128), 0, s, a);
+    return hipGetLastError();
+  }
   const int64_t grid = (int64_t)a.B * a.Hkv * a.nsplit;
   if (grid == 0) return hipSuccess;
   if (a.ring_n)
-    hipLaunchKernelGGL(decode_split_bf16_d128<true>, dim3((unsigned)grid), dim3(64), 0, s, a);
+    hipLaunchKernelGGL((decode_split_bf16_d128<true, false>), dim3((unsigned)grid), dim3(64), 0, s, a);
   else
-    hipLaunchKernelGGL(decode_split_bf16_d128<false>, dim3((unsigned)grid), dim3(64), 0, s, a);
+    hipLaunchKernelGGL((decode_split_bf16_d128<false, false>), dim3((unsigned)grid), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 

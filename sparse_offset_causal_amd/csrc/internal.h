@@ -31,6 +31,8 @@ struct AttnArgs {
   int32_t nsplit;  // splits per sequence (capacity)
   int32_t split;   // keys per split
   int32_t lpt;     // bf16 decode: workgroups take the splits longest first (grids of several rounds)
+  int32_t fused;   // bf16 ring decode with nsplit <= 2: one workgroup per (sequence, KV head) merges
+                   // its two splits itself and writes the output (no partials, no merge kernel)
   // ring-buffer decode (bf16): the cache is a tk-slot ring per (sequence, KV head), ring_n[b]
   // tokens written before this step; the step's K/V rows (k_new, v_new) go to slot
   // ring_n[b] % tk, and the step attends over the min(ring_n[b] + 1, tk) filled slots.

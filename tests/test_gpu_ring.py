@@ -54,12 +54,17 @@ def test_ring_decode_f32_steps_match_both_oracle_routes(with_sink, split):
     assert worst_ring <= F32_TOL and worst_mask <= F32_TOL, (worst_ring, worst_mask)
 
 
-def test_ring_decode_bf16_staggered_sequences():
-    announce("ring bf16 staggered")
+@pytest.mark.parametrize("split,with_sink", [(24, True), (32, True), (64, True), (32, False)])
+def test_ring_decode_bf16_staggered_sequences(split, with_sink):
+    """split 24: three splits per ring (split kernel + merge kernel); 32: two splits merged
+    inside one workgroup; 64: one split, its workgroup's second wave empty."""
+    announce(f"ring bf16 staggered split={split} sink={with_sink}")
     B, Hq, Hkv, d, W = 3, 32, 8, 128, 64
     # empty, partly filled and wrapped rings; unwritten slots hold stale values
     st = synth.ring_state(B, Hq, Hkv, d, W, seed=5, n_seen=[0, 37, 300])
-    k_ring, v_ring, n_seen, sink = dev(st.k), dev(st.v), dev(st.n_seen), dev(st.sink)
+    k_ring, v_ring, n_seen = dev(st.k), dev(st.v), dev(st.n_seen)
+    sink = dev(st.sink) if with_sink else None
+    sink64 = host64(st.sink) if with_sink else None
     rings = []
     for b in range(B):
         r = RingCache(Hkv, d, W)
@@ -68,12 +73,11 @@ def test_ring_decode_bf16_staggered_sequences():
     worst = 0.0
     for t in range(90):
         q, kn, vn = synth.ring_step(B, Hq, Hkv, d, t, seed=5)
-        o = attn_ring_decode(dev(q), dev(kn), dev(vn), k_ring, v_ring, n_seen, sink=sink, split_tokens=24)
+        o = attn_ring_decode(dev(q), dev(kn), dev(vn), k_ring, v_ring, n_seen, sink=sink, split_tokens=split)
         n_seen += 1
         for b in range(B):
             K, V = rings[b].add(host64(kn[b, :, 0]), host64(vn[b, :, 0]))
-            worst = max(worst, max_abs(o[b, :, 0], attend_unmasked(host64(q[b, :, 0]), K, V, Hq,
-                                                                   sink=host64(st.sink))))
+            worst = max(worst, max_abs(o[b, :, 0], attend_unmasked(host64(q[b, :, 0]), K, V, Hq, sink=sink64)))
     for b in range(B):
         filled = min(rings[b].n, W)
         assert np.array_equal(host64(k_ring[b, :, :filled]), rings[b].k[:, :filled])
