@@ -144,8 +144,18 @@ prefill_bf16_d128(AttnArgs a) {
   } else {
     n1 = max(0, t_hi - t_lo);
   }
+  // Sparse mode keeps the list in registers, 64 entries per load (lane j holds entry
+  // lchunk + j), so a tile's index is a lane read rather than a memory round trip that would
+  // sit between a tile's start and its successor's DMA.
+  int lchunk = -64, lreg = 0;
   auto tile_of = [&](int n) __attribute__((always_inline)) -> int {
-    return SPARSE ? __builtin_amdgcn_readfirstlane(2 * lst[1 + (n >> 1)] + (n & 1)) : t_lo + n;
+    if (!SPARSE) return t_lo + n;
+    const int e = n >> 1;
+    if ((e & ~63) != lchunk) {  // uniform; once per 64 list entries
+      lchunk = e & ~63;
+      lreg = lchunk + lane < ((n1 + 1) >> 1) ? lst[1 + lchunk + lane] : 0;
+    }
+    return 2 * __builtin_amdgcn_readlane(lreg, e & 63) + (n & 1);
   };
 
   // HBM -> LDS for one tile: wave w fills 1 KB blocks 4w..4w+3 (rows 16w..16w+15) of K and V.
