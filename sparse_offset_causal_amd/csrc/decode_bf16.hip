@@ -91,8 +91,10 @@ __device__ bool lpt_item(const AttnArgs& a, int item, int* hist, int& b_out, int
     s_lo = nsb = sf0 = nfull = p1 = p2 = 0;
     if (bb >= a.B) return;
     const int off = seq_cache_off(a, bb);
-    const int tkb = off + a.tq;
-    const int kv_lo = a.window > 0 ? max(0, off - a.window + 1) : 0;
+    // never a split index past the workspace's nsplit, whatever the offsets hold (a valid
+    // offset has off + tq <= tk <= nsplit * split, so this changes nothing for those)
+    const int tkb = min(off + a.tq, a.nsplit * a.split);
+    const int kv_lo = a.window > 0 ? max(0, min(off - a.window + 1, tkb - 1)) : 0;
     nsb = (tkb + a.split - 1) / a.split;
     s_lo = kv_lo / a.split;
     const int bf = (min((s_lo + 1) * a.split, tkb) - kv_lo + KB - 1) / KB;
