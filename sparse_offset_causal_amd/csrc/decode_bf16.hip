@@ -451,7 +451,8 @@ __global__ void __launch_bounds__(64) decode_merge(AttnArgs a) {
   const int b = (int)(rowid / ((int64_t)a.tq * a.Hq));
   const int off = seq_cache_off(a, b);
   const int tkb = off + a.tq;
-  const int nsb = __builtin_amdgcn_readfirstlane((tkb + a.split - 1) / a.split);
+  // splits written for this row (never more than the workspace holds, whatever the offset)
+  const int nsb = __builtin_amdgcn_readfirstlane(min((tkb + a.split - 1) / a.split, a.nsplit));
   const float* pml = a.part + decode_o_floats(a) + rowid * a.nsplit * 2;
   const float* po = a.part + rowid * a.nsplit * a.d;
   float M = SOC_NEG_INF;

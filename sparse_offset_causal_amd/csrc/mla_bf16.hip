@@ -297,7 +297,7 @@ __global__ void __launch_bounds__(256) mla_merge_kernel(MlaArgs a) {
   const int R = a.H * a.tq;
   const int b = row / R, t = (row % R) % a.tq;
   const int off = a.cache_off ? a.cache_off[b] : a.tk - a.tq;
-  const int nsb = (off + a.tq + a.split - 1) / a.split;
+  const int nsb = min((off + a.tq + a.split - 1) / a.split, a.nsplit);  // never past the workspace
   const int64_t p0 = (int64_t)row * a.nsplit;
   (void)t;
   if (threadIdx.x < 64) {  // wave 0: max over splits, then the weights and their sum
