@@ -75,6 +75,10 @@ PREFILL_CASES = [
     (1, 8, 2, 64, 64, None, 1, False),
     (3, 8, 8, 190, 450, [0, 100, 260], 77, True),
     (1, 16, 8, 1024, 1536, None, 0, False),
+    # windowed GQA: g = 2 and g = 6 stack two heads over 64 rows, g = 3 stacks rows only
+    (2, 4, 2, 333, 900, [100, 567], 150, True),
+    (1, 12, 2, 200, 500, [300], 64, True),
+    (1, 6, 2, 250, 250, None, 40, False),
 ]
 
 
