@@ -87,7 +87,7 @@ __device__ __forceinline__ int wave_incl_prefix_i(int x) {
   return x;
 }
 
-__global__ void __launch_bounds__(64) dsa_indexer_kernel(DsaArgs A) {
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) dsa_indexer_kernel(DsaArgs A) {
   const AttnArgs& a = A.at;
   const int lane = threadIdx.x, G = lane >> 4, i16 = lane & 15;
   const int rows = a.B * a.tq;
@@ -142,6 +142,7 @@ __global__ void __launch_bounds__(64) dsa_indexer_kernel(DsaArgs A) {
     const bf16_t* kp = (const bf16_t*)A.ki + b * A.ki_sb;
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kp, (short)0, (int)(n_vis * row_bytes), 0x00020000);
     float* out = A.scores + ((int64_t)b * a.tq + t) * a.tk;
+    const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc((void*)out, (short)0, (int)(n_vis * 4), 0x00020000);
     const int j0 = g - rstart, j1 = min(nb_row, hi - rstart);  // this wave's blocks of the row
     auto load = [&](bf16x8* af, int j) __attribute__((always_inline)) {
       const int tok0 = 16 * j;
@@ -162,26 +163,36 @@ __global__ void __launch_bounds__(64) dsa_indexer_kernel(DsaArgs A) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) part[v] = fmaf(w[hb], fmaxf(acc[v], 0.f), part[v]);
       }
-      // lane (G, i16): tokens 4G + v, indexer head i16 of each block; sum over the 16 heads
+      // lane (G, i16): tokens 4G + v, indexer head i16 of each block; sum over the 16 heads.
+      // Lane i16 == 0 of each group stores through a buffer whose range ends at the row's
+      // last visible token; the other lanes' stores fall outside the range and are dropped
+      // (no branch, so the compiler can keep counting the key loads still in flight).
 #pragma unroll
       for (int v = 0; v < 4; ++v) part[v] = row16_sum(part[v]);
-      if (i16 == 0) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int tok = tok0 + 4 * G + v;
-          if (tok < n_vis) out[tok] = part[v];
-        }
+      for (int v = 0; v < 4; ++v) {
+        const uint32_t at = i16 == 0 ? (uint32_t)(tok0 + 4 * G + v) * 4u : 0x80000000u;
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, part[v]), ors, at, 0, 0);
       }
     };
-    // the keys of block j + 1 are in flight while block j is scored
-    bf16x8 fa[4], fb[4];
-    load(fa, j0);
-    for (int j = j0; j < j1; j += 2) {
-      if (j + 1 < j1) load(fb, j + 1);
+    // the keys of blocks j + 1 and j + 2 are in flight while block j is scored (three
+    // rotating buffers; with one block ahead the waves held too few bytes in flight to
+    // cover the memory latency)
+    // Every load is issued unconditionally (past the segment's last block it reloads that
+    // block), so the number of loads in flight is the same on every path.
+    bf16x8 fa[4], fb[4], fc[4];
+    const int jl = j1 - 1;
+    load(fa, min(j0, jl));
+    load(fb, min(j0 + 1, jl));
+    for (int j = j0; j < j1; j += 3) {
+      load(fc, min(j + 2, jl));
       score(fa, j);
       if (j + 1 >= j1) break;
-      if (j + 2 < j1) load(fa, j + 2);
+      load(fa, min(j + 3, jl));
       score(fb, j + 1);
+      if (j + 2 >= j1) break;
+      load(fb, min(j + 4, jl));
+      score(fc, j + 2);
     }
     g = rstart + j1;
     rstart += nb_row;
