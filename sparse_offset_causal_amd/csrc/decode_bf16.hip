@@ -273,8 +273,14 @@ decode_split_bf16_d128(AttnArgs a) {
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // only block loads are counted below
 
-  if (nblk > 0) issue(0, std::integral_constant<int, 0>{});
-  if (nblk > 1) issue(1, std::integral_constant<int, 1>{});
+  // Every step issues one block (past the last block it issues the last block again, into a
+  // stage already consumed), so exactly NST - 1 blocks are younger than the one a step
+  // consumes on every path; with the issue behind a condition the compiler could not count
+  // the loads in flight at the loop head and drained them all there, once per NST blocks.
+  if (nblk > 0) {
+    issue(0, std::integral_constant<int, 0>{});
+    issue(min(1, nblk - 1), std::integral_constant<int, 1>{});
+  }
 
   f32x16 oacc[4];
 #pragma unroll
@@ -297,8 +303,8 @@ decode_split_bf16_d128(AttnArgs a) {
 
   auto step = [&](int n, auto stage_tag) __attribute__((always_inline)) {
     constexpr int ST = decltype(stage_tag)::value;
-    if (n + NST - 1 < nblk) issue(n + NST - 1, std::integral_constant<int, (ST + NST - 1) % NST>{});
-    wait_blocks(min(NST - 1, nblk - 1 - n));
+    issue(min(n + NST - 1, nblk - 1), std::integral_constant<int, (ST + NST - 1) % NST>{});
+    wait_blocks(NST - 1);
     const bf16_t* vt = vbase + ST * VSTAGE;
     const int js = kbeg + n * KB;
     if (RING && own_slot && slot >= js && slot < js + KB) {  // uniform: the ring slot being overwritten
@@ -357,11 +363,15 @@ decode_split_bf16_d128(AttnArgs a) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this stage's LDS reads finish before its refill
   };
 
-  for (int n = 0; n < nblk; n += NST) {
+  int n = 0;
+  for (; n + NST <= nblk; n += NST) {
     step(n, std::integral_constant<int, 0>{});
-    if (n + 1 < nblk) step(n + 1, std::integral_constant<int, 1>{});
-    if (n + 2 < nblk) step(n + 2, std::integral_constant<int, 2>{});
+    step(n + 1, std::integral_constant<int, 1>{});
+    step(n + 2, std::integral_constant<int, 2>{});
   }
+  if (n < nblk) step(n, std::integral_constant<int, 0>{});
+  if (n + 1 < nblk) step(n + 1, std::integral_constant<int, 1>{});
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the repeated last blocks land before LDS reuse or exit
 
   const float L = pair_sum(l_run);
   if constexpr (FUSED) {
