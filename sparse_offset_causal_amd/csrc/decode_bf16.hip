@@ -56,15 +56,21 @@ typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
 
 __device__ __forceinline__ int v_off(int row, int chunk) { return row * D + ((chunk ^ ((row & 3) << 2)) << 3); }
 
-// Wait until at most `blocks_after` blocks (16 loads each: 8 of K, 8 of V) are still in flight.
-__device__ __forceinline__ void wait_blocks(int blocks_after) {
-  static_assert(NST - 1 <= 3, "vmcnt holds at most 63 outstanding loads: 3 blocks of 16");
-  if (blocks_after >= 2)
-    asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
-  else if (blocks_after == 1)
-    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-  else
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+// s_waitcnt vmcnt(N) through the builtin rather than inline assembly: the compiler's own wait
+// insertion then knows these loads have landed (it cannot read an asm statement) and adds no
+// waits of its own for them.  gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4 and
+// lgkmcnt 11:8 left at their maxima (no wait).
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N <= 63, "vmcnt counts at most 63 loads");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Wait until at most `BLOCKS_AFTER` blocks (16 loads each: 8 of K, 8 of V) are still in flight.
+template <int BLOCKS_AFTER>
+__device__ __forceinline__ void wait_blocks() {
+  static_assert(BLOCKS_AFTER <= 3, "vmcnt holds at most 63 outstanding loads: 3 blocks of 16");
+  vm_wait<16 * BLOCKS_AFTER>();
 }
 
 __device__ __forceinline__ int wave_incl_prefix(int x) {
@@ -271,7 +277,7 @@ decode_split_bf16_d128(AttnArgs a) {
     u32x4 z = {0u, 0u, 0u, 0u};
     qf[ks] = row_ok ? *(const bf16x8*)(qp + 16 * ks + 8 * hh) : as_bf16x8(z);
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // only block loads are counted below
+  vm_wait<0>();  // only block loads are counted below
 
   // Every step issues one block (past the last block it issues the last block again, into a
   // stage already consumed), so exactly NST - 1 blocks are younger than the one a step
@@ -304,7 +310,7 @@ decode_split_bf16_d128(AttnArgs a) {
   auto step = [&](int n, auto stage_tag) __attribute__((always_inline)) {
     constexpr int ST = decltype(stage_tag)::value;
     issue(min(n + NST - 1, nblk - 1), std::integral_constant<int, (ST + NST - 1) % NST>{});
-    wait_blocks(NST - 1);
+    wait_blocks<NST - 1>();
     const bf16_t* vt = vbase + ST * VSTAGE;
     const int js = kbeg + n * KB;
     if (RING && own_slot && slot >= js && slot < js + KB) {  // uniform: the ring slot being overwritten
@@ -371,7 +377,7 @@ decode_split_bf16_d128(AttnArgs a) {
   }
   if (n < nblk) step(n, std::integral_constant<int, 0>{});
   if (n + 1 < nblk) step(n + 1, std::integral_constant<int, 1>{});
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the repeated last blocks land before LDS reuse or exit
+  vm_wait<0>();  // the repeated last blocks land before LDS reuse or exit
 
   const float L = pair_sum(l_run);
   if constexpr (FUSED) {

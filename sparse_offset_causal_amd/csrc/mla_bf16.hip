@@ -15,8 +15,10 @@
 //                           that take (sequence, group of 16 query rows, split of keys) items
 //                           from an atomic queue; the 16 rows (heads x query tokens) are the N
 //                           columns of the MFMAs.  The four waves share the ring: each loads a
-//                           quarter of every block, computes the (cheap) scores in full and
-//                           a quarter of the 512-dim latent output.  Latent rows go HBM ->
+//                           quarter of every block, computes a quarter of the 576-dim score
+//                           contraction (the partial score blocks are summed through LDS, in a
+//                           fixed order, so every wave holds the same scores) and a quarter of
+//                           the 512-dim latent output.  Latent rows go HBM ->
 //                           registers (two 16-key blocks ahead) -> LDS (a 2-stage ring,
 //                           16-byte chunks XOR-swizzled by key); S^T = [C, R] [q_lat, q_rope]^T with
 //                           v_mfma_f32_16x16x32_bf16 over 576 dims; online softmax in the log2
@@ -95,14 +97,25 @@ __global__ void __launch_bounds__(64) mla_absorb_q_kernel(MlaArgs a) {
 // ---------------------------------------------------------------------------------------
 // Loads per wave per block: 4 latent rows (1 KB each) and a quarter (512 B) of the rope tile.
 constexpr int WAVE_LOADS = 5;
+// s_waitcnt vmcnt(N) through the builtin rather than inline assembly: the compiler's own wait
+// insertion then knows these loads have landed and adds no waits of its own for them (it
+// cannot read an asm statement, and without that it drained every load before the first
+// use of the query fragments in each block).  gfx9 encoding: vmcnt in bits 3:0 and 15:14,
+// expcnt 6:4 and lgkmcnt 11:8 left at their maxima (no wait).
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N <= 63, "vmcnt counts at most 63 loads");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 template <int AFTER>
 __device__ __forceinline__ void wait_wave_blocks() {
   static_assert(AFTER * WAVE_LOADS <= 63, "vmcnt counts at most 63 loads");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(AFTER * WAVE_LOADS) : "memory");
+  vm_wait<AFTER * WAVE_LOADS>();
 }
 
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) mla_split_kernel(MlaArgs a) {
   __shared__ __attribute__((aligned(1024))) bf16_t lds[MNST * MSTAGE];
+  __shared__ __attribute__((aligned(16))) float xs[4][64][4];  // each wave's partial score block
   __shared__ uint32_t item_sh;
 
   const int tid = threadIdx.x, lane = tid & 63, G = lane >> 4, i16 = lane & 15;
@@ -112,15 +125,16 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) m
   const uint32_t n_items = (uint32_t)a.B * nrg * a.nsplit;
 
   // fixed per-lane LDS element offsets
-  //   S A operand (key i16 of the block, chunk 4ks + G): i16*512 + ((4ks + G) ^ i16) * 8
-  //   rope A operand (key i16, chunk 4kr + G):          i16*64 + ((4kr + G) ^ (i16 & 7)) * 8
+  //   S A operand (key i16 of the block, chunk 4ks + G): i16*512 + ((4ks + G) ^ i16) * 8.
+  //     Wave w takes the latent dim chunks ks = w + 4j (j < 4): the swizzle touches only the
+  //     low four chunk bits, so chunk ks sits at lat_b + 128 j
+  //   rope A operand (key i16, chunk 4kr + G):          i16*64 + ((4kr + G) ^ (i16 & 7)) * 8,
+  //     rope chunk kr = w for waves 0 and 1
   //   PV A operand, ds_read_b64_tr_b16 (lane j of group G: key 4G + j/4, dims 16db + 4(j%4)..+3):
   //   with db = 8u + w this wave's dim blocks are u = wave, offset trb[w] + wave*128
-  int lat_s[16], rope_s[2], trb[8];
-#pragma unroll
-  for (int ks = 0; ks < 16; ++ks) lat_s[ks] = i16 * 512 + (((4 * ks + G) ^ i16) << 3);
-#pragma unroll
-  for (int kr = 0; kr < 2; ++kr) rope_s[kr] = i16 * 64 + (((4 * kr + G) ^ (i16 & 7)) << 3);
+  int trb[8];
+  const int lat_b = i16 * 512 + (((4 * wave + G) ^ i16) << 3);
+  const int rope_b = i16 * 64 + (((4 * (wave & 1) + G) ^ (i16 & 7)) << 3);
   {
     const int kk = 4 * G + (i16 >> 2);
     const int x = (i16 & 3) >> 1;
@@ -130,7 +144,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) m
   // DMA lane offsets: latent row of key i goes to LDS row i (1 KB), LDS chunk j holding the
   // row's chunk j ^ i; the rope tile holds key k's chunk j ^ (k & 7) at chunk j.  Wave w loads
   // latent rows 4w..4w+3 and rope keys 4w..4w+3 (lanes 0..31).
-  const uint32_t rope_key = 4u * wave + (uint32_t)(lane >> 3);
+  const uint32_t rope_key = 4u * wave + (uint32_t)((lane & 31) >> 3);  // lanes 32..63 repeat lanes 0..31
   const float c = a.scale_log2;
 
   for (;;) {
@@ -172,7 +186,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) m
       for (int i = 0; i < 4; ++i)
         stg[BUF][i] = __builtin_amdgcn_raw_buffer_load_b128(crs, (uint32_t)(4 * wave + i) * crow + (uint32_t)(16 * lane),
                                                             k0 * crow, 0);
-      if (lane < 32) stg[BUF][4] = __builtin_amdgcn_raw_buffer_load_b128(rrs, rope_v, k0 * rrow, 0);
+      // every lane loads (lanes 32..63 the same bytes as lanes 0..31, one request per line), so
+      // a block is always WAVE_LOADS loads and the compiler can count them
+      stg[BUF][4] = __builtin_amdgcn_raw_buffer_load_b128(rrs, rope_v, k0 * rrow, 0);
     };
     // registers -> LDS stage, XOR-swizzled in 16-byte chunks by key
     auto store = [&](auto buf_tag) __attribute__((always_inline)) {
@@ -187,21 +203,28 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) m
       if (lane < 32) *(u32x4*)(rop + rope_key * 64 + (((lane & 7) ^ (rope_key & 7)) << 3)) = stg[BUF][4];
     };
 
-    // query fragments (B operand of S^T): dims 32ks + 8G .. +7 of row rho; 16 latent steps, 2 rope steps
-    bf16x8 qf[18];
+    // query fragments (B operand of S^T): dims 32ks + 8G .. +7 of row rho for this wave's
+    // latent chunks ks = wave + 4j, then its rope chunk (used by waves 0 and 1)
+    bf16x8 qf[5];
     {
       const bf16_t* ql = (const bf16_t*)a.q_lat + ((int64_t)b * R + rho) * MR;
       const bf16_t* qr = (const bf16_t*)a.q_rope + b * a.qr_sb + h * a.qr_sh + t * a.qr_st;
       const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int ks = 0; ks < 16; ++ks) qf[ks] = row_ok ? *(const bf16x8*)(ql + 32 * ks + 8 * G) : as_bf16x8(z);
-#pragma unroll
-      for (int kr = 0; kr < 2; ++kr) qf[16 + kr] = row_ok ? *(const bf16x8*)(qr + 32 * kr + 8 * G) : as_bf16x8(z);
+      for (int j = 0; j < 4; ++j) qf[j] = row_ok ? *(const bf16x8*)(ql + 32 * (wave + 4 * j) + 8 * G) : as_bf16x8(z);
+      qf[4] = row_ok ? *(const bf16x8*)(qr + 32 * (wave & 1) + 8 * G) : as_bf16x8(z);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // only block loads are counted below
+    vm_wait<0>();  // only block loads are counted below
 
-    if (nblk > 0) issue(0, std::integral_constant<int, 0>{});
-    if (nblk > 1) issue(1, std::integral_constant<int, 1>{});
+    // Every step issues one block (past the last block it issues the last block again into
+    // the registers it just stored), so exactly one block is younger than the one a step
+    // stores on every path.  With the issues and waits behind conditions the compiler could
+    // not count the loads in flight and drained them all once every two blocks.
+    if (nblk > 0) {
+      issue(0, std::integral_constant<int, 0>{});
+      __builtin_amdgcn_sched_barrier(0);  // block 0's loads stay ahead of block 1's (the waits count on it)
+      issue(min(1, nblk - 1), std::integral_constant<int, 1>{});
+    }
 
     f32x4 oacc[8];
 #pragma unroll
@@ -210,23 +233,27 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) m
 
     auto step = [&](int n, auto stage_tag) __attribute__((always_inline)) {
       constexpr int ST = decltype(stage_tag)::value;
-      // block n+1 (issued earlier) may stay in flight; block n's registers must have landed
-      if (n + 1 < nblk) wait_wave_blocks<1>();
-      else wait_wave_blocks<0>();
+      wait_wave_blocks<1>();  // block n+1 (issued earlier) may stay in flight; block n's registers have landed
       store(std::integral_constant<int, ST>{});  // stage ST held block n-2: every wave finished it before barrier n-1
-      if (n + 2 < nblk) issue(n + 2, std::integral_constant<int, ST>{});  // the registers just stored
+      issue(min(n + 2, nblk - 1), std::integral_constant<int, ST>{});  // the registers just stored
       __syncthreads();  // every wave's part of block n is in LDS
       const bf16_t* lat = lds + ST * MSTAGE;
       const bf16_t* rop = lat + LAT_STAGE;
 
+      // this wave's share of the score contraction: latent chunks wave + 4j, rope chunk wave
       f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 16; ks += 2) {
-        s0 = mfma16k32(*(const bf16x8*)(lat + lat_s[ks]), qf[ks], s0);
-        s1 = mfma16k32(*(const bf16x8*)(lat + lat_s[ks + 1]), qf[ks + 1], s1);
-      }
-      s0 = mfma16k32(*(const bf16x8*)(rop + rope_s[0]), qf[16], s0);
-      s1 = mfma16k32(*(const bf16x8*)(rop + rope_s[1]), qf[17], s1);
+      s0 = mfma16k32(*(const bf16x8*)(lat + lat_b), qf[0], s0);
+      s1 = mfma16k32(*(const bf16x8*)(lat + lat_b + 128), qf[1], s1);
+      s0 = mfma16k32(*(const bf16x8*)(lat + lat_b + 256), qf[2], s0);
+      s1 = mfma16k32(*(const bf16x8*)(lat + lat_b + 384), qf[3], s1);
+      if (wave < 2) s0 = mfma16k32(*(const bf16x8*)(rop + rope_b), qf[4], s0);
+      // partial blocks summed through LDS in wave order, so every wave gets the same scores;
+      // xs is rewritten only after the next block's barrier, which every wave reaches after
+      // its reads below
+      *(f32x4*)&xs[wave][lane][0] = s0 + s1;
+      __syncthreads();
+      const f32x4 sc = ((*(const f32x4*)&xs[0][lane][0] + *(const f32x4*)&xs[1][lane][0]) +
+                        *(const f32x4*)&xs[2][lane][0]) + *(const f32x4*)&xs[3][lane][0];
       // lane: keys 4G + v of the block for row i16 (every wave holds the whole score block)
       const int j0 = ks0 + n * MKB + 4 * G;
       float sv[4];
@@ -234,7 +261,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) m
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int j = j0 + v;
-        sv[v] = (j < ks1 && j <= pos) ? s0[v] + s1[v] : SOC_NEG_INF;
+        sv[v] = (j < ks1 && j <= pos) ? sc[v] : SOC_NEG_INF;
         mx = fmaxf(mx, sv[v]);
       }
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
@@ -267,10 +294,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) m
       }
     };
 
-    for (int n = 0; n < nblk; n += MNST) {
+    static_assert(MNST == 2, "the buffer rotation below is written for two stages");
+    int n = 0;
+    for (; n + MNST <= nblk; n += MNST) {
       step(n, std::integral_constant<int, 0>{});
-      if (n + 1 < nblk) step(n + 1, std::integral_constant<int, 1>{});
+      step(n + 1, std::integral_constant<int, 1>{});
     }
+    if (n < nblk) step(n, std::integral_constant<int, 0>{});
+    vm_wait<0>();  // the repeated last block lands before the registers are reused
 
     // the row's sum over the 4 lanes that share it
     l_run += __shfl_xor(l_run, 16, 64);
