@@ -368,7 +368,8 @@ __global__ void __launch_bounds__(256) mla_merge_kernel(MlaArgs a) {
 // o[row, 32q + j] = sum_r o_lat[row, r] w_uv[h, r, 32q + j] for 16 rows (b, t) of head h
 // (grid: H x row groups x 4 quarters of the output width).
 __global__ void __launch_bounds__(256) mla_expand_kernel(MlaArgs a) {
-  __shared__ __attribute__((aligned(16))) float ol[16][MR];
+  __shared__ __attribute__((aligned(16))) float ol[16][MR + 4];  // rows padded: 16 rows hit 16 bank groups
+  __shared__ __attribute__((aligned(16))) float part[16][32];    // upper latent half's partial products
   __shared__ __attribute__((aligned(16))) bf16_t ws[MR][32];  // w_uv[h][:, 32 q4 .. 32 q4 + 31]
   const int q4 = blockIdx.x & 3;
   const int hg = blockIdx.x >> 2;
@@ -401,21 +402,34 @@ __global__ void __launch_bounds__(256) mla_expand_kernel(MlaArgs a) {
     }
   }
   __syncthreads();
-  const int j = threadIdx.x & 31, rp = threadIdx.x >> 5;  // output dim 32 q4 + j, rows 2 rp, 2 rp + 1
-  const int dout = 32 * q4 + j;
-  float a0 = 0.f, a1 = 0.f;
+  // o[16 rows][32 dims] = ol[16][512] ws[512][32] in fp32 with v_mfma_f32_16x16x4f32 (lane l:
+  // A[l%16][l/16], B[l/16][l%16], D[4(l/16)+v][l%16]); wave w takes output dims 16 (w & 1) ..
+  // over latent half w >> 1, in two accumulator chains; the upper half's products go through LDS
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int jt = wv & 1, kh = wv >> 1;
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
-  for (int r = 0; r < MR; ++r) {
-    const float w = (float)ws[r][j];
-    a0 = fmaf(ol[2 * rp][r], w, a0);
-    a1 = fmaf(ol[2 * rp + 1][r], w, a1);
+  for (int k0 = 256 * kh; k0 < 256 * kh + 256; k0 += 8) {
+    acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ol[lane & 15][k0 + (lane >> 4)], (float)ws[k0 + (lane >> 4)][16 * jt + (lane & 15)],
+                                                acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(ol[lane & 15][k0 + 4 + (lane >> 4)],
+                                                (float)ws[k0 + 4 + (lane >> 4)][16 * jt + (lane & 15)], acc1, 0, 0, 0);
   }
+  const f32x4 acc = acc0 + acc1;  // rows 4 (lane/16) + v, dim 16 jt + lane % 16
+  if (kh == 1) {
 #pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const int idx = grp * 16 + 2 * rp + e;
-    if (idx < nrow) {
-      const int b = idx / a.tq, t = idx % a.tq;
-      ((bf16_t*)a.o)[b * a.o_sb + h * a.o_sh + t * a.o_st + dout] = (bf16_t)(e ? a1 : a0);
+    for (int v = 0; v < 4; ++v) part[4 * (lane >> 4) + v][16 * jt + (lane & 15)] = acc[v];
+  }
+  __syncthreads();
+  if (kh == 0) {
+    const int dout = 32 * q4 + 16 * jt + (lane & 15);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int r = 4 * (lane >> 4) + v, idx = grp * 16 + r;
+      if (idx < nrow) {
+        const int b = idx / a.tq, t = idx % a.tq;
+        ((bf16_t*)a.o)[b * a.o_sb + h * a.o_sh + t * a.o_st + dout] = (bf16_t)(acc[v] + part[r][16 * jt + (lane & 15)]);
+      }
     }
   }
 }
