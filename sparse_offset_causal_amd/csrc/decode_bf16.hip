@@ -19,6 +19,22 @@
 // than 2^8).  The split's unnormalised partial (max, sum, O) is written in fp32.  The sink is
 // not applied here; the merge adds it exactly once per row.
 //
+// Ordering.  Every wait is in the source, through the s_waitcnt builtin, which the compiler
+// treats as touching all memory, so no LDS access moves across it:
+//   * a block's K registers and V stage are complete before the step that consumes them
+//     reads them or (ring mode) writes its stage.  Loads into registers and LDS-DMA loads
+//     each retire in issue order, but not in order with each other: a wait that counted
+//     them as one ordered stream (at most the younger blocks' 32 loads outstanding) let a
+//     stage's own DMA land after the step had written the ring's new V row into it.  So a
+//     step waits until at most 16 loads are outstanding: if any of block n's 8 K or 8 V
+//     loads were still pending, the 16 loads of the same kind issued after it (blocks n+1
+//     and n+2) would be pending too.  One younger block stays in flight.
+//   * a stage's transposed reads have completed before the DMA that refills it is issued:
+//     each step ends with lgkmcnt(0).
+// Each stage is a separate LDS variable, so the compiler can tell which stage a pending DMA
+// writes and adds no wait of its own (with the three stages in one array it drained every
+// load before each block's V reads).
+//
 // Work order: when the grid takes several rounds of the chip, workgroup i does not take the
 // i-th (sequence, KV head, split) in grid order but the i-th in longest-first order: every
 // full split, then the partial splits by block count (largest first), then the empty splits
@@ -66,12 +82,17 @@ __device__ __forceinline__ void vm_wait() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Wait until at most `BLOCKS_AFTER` blocks (16 loads each: 8 of K, 8 of V) are still in flight.
+// Block n's loads have all retired, `BLOCKS_AFTER` younger blocks (8 K and 8 V loads each)
+// having been issued since: at most 8 * BLOCKS_AFTER loads may then be outstanding (each kind
+// retires in order within itself only).
 template <int BLOCKS_AFTER>
 __device__ __forceinline__ void wait_blocks() {
-  static_assert(BLOCKS_AFTER <= 3, "vmcnt holds at most 63 outstanding loads: 3 blocks of 16");
-  vm_wait<16 * BLOCKS_AFTER>();
+  static_assert(16 * BLOCKS_AFTER <= 63, "vmcnt holds at most 63 outstanding loads");
+  vm_wait<8 * BLOCKS_AFTER>();
 }
+
+// s_waitcnt lgkmcnt(0): every LDS access of this wave has completed.
+__device__ __forceinline__ void lds_wait() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
 
 __device__ __forceinline__ int wave_incl_prefix(int x) {
   const int lane = threadIdx.x & 63;
@@ -186,12 +207,21 @@ template <bool RING, bool FUSED>
 __global__ void __launch_bounds__(FUSED ? 128 : 64) __attribute__((amdgpu_waves_per_eu(2)))
 decode_split_bf16_d128(AttnArgs a) {
   constexpr int NW = FUSED ? 2 : 1;  // waves (splits) per workgroup
-  __shared__ __attribute__((aligned(1024))) bf16_t vlds[NW * NST * VSTAGE];
+  static_assert(NST == 3, "one LDS variable per stage");
+  __shared__ __attribute__((aligned(1024))) bf16_t vst0[NW * VSTAGE];
+  __shared__ __attribute__((aligned(1024))) bf16_t vst1[NW * VSTAGE];
+  __shared__ __attribute__((aligned(1024))) bf16_t vst2[NW * VSTAGE];
 
   const int lane = threadIdx.x & 63;
   const int wave = FUSED ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
   const int l32 = lane & 31, hh = lane >> 5;
-  bf16_t* const vbase = vlds + wave * (NST * VSTAGE);  // this wave's V stages
+  // V stage ST; this wave's part of it starts wofs elements in (folded into the per-lane
+  // read offsets, so that each stage's base stays a constant of the instruction)
+  auto vstage = [&](auto stage_tag) __attribute__((always_inline)) -> bf16_t* {
+    constexpr int ST = decltype(stage_tag)::value;
+    return ST == 0 ? vst0 : ST == 1 ? vst1 : vst2;
+  };
+  const int wofs = wave * VSTAGE;
   int s_i, kvh_i, b_i;
   if constexpr (FUSED) {
     s_i = wave;
@@ -260,7 +290,7 @@ decode_split_bf16_d128(AttnArgs a) {
       kreg[ST][ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(krs, k_lane + ks * 32, blk_off, 0));
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void_ptr)(vbase + ST * VSTAGE + i * 512), 16, v_lane,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void_ptr)(vstage(stage_tag) + wofs + i * 512), 16, v_lane,
                                                blk_off + 4 * i * row_bytes, 0, 0);
   };
 
@@ -303,15 +333,15 @@ decode_split_bf16_d128(AttnArgs a) {
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
       const int col = tb * 32 + tr_col;
-      voff[tb] = v_off(tr_row, col >> 3) + (col & 7);
+      voff[tb] = wofs + v_off(tr_row, col >> 3) + (col & 7);
     }
   }
 
   auto step = [&](int n, auto stage_tag) __attribute__((always_inline)) {
     constexpr int ST = decltype(stage_tag)::value;
     issue(min(n + NST - 1, nblk - 1), std::integral_constant<int, (ST + NST - 1) % NST>{});
-    wait_blocks<NST - 1>();
-    const bf16_t* vt = vbase + ST * VSTAGE;
+    wait_blocks<NST - 1>();  // block n's K registers and V stage have landed
+    const bf16_t* vt = vstage(stage_tag);
     const int js = kbeg + n * KB;
     if (RING && own_slot && slot >= js && slot < js + KB) {  // uniform: the ring slot being overwritten
       const int rr = slot - js;
@@ -319,7 +349,7 @@ decode_split_bf16_d128(AttnArgs a) {
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) kreg[ST][ks] = *(const bf16x8*)(&newrow[0][16 * ks + 8 * hh]);
       }
-      if (lane < 16) *(u32x4*)(const_cast<bf16_t*>(vt) + v_off(rr, lane)) = *(const u32x4*)(&newrow[1][8 * lane]);
+      if (lane < 16) *(u32x4*)(const_cast<bf16_t*>(vt) + wofs + v_off(rr, lane)) = *(const u32x4*)(&newrow[1][8 * lane]);
     }
 
     f32x16 sacc;
@@ -366,7 +396,7 @@ decode_split_bf16_d128(AttnArgs a) {
         const s16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         oacc[tb] = mfma32x32x16(__builtin_bit_cast(bf16x8, va), pb[kk], oacc[tb]);
       }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this stage's LDS reads finish before its refill
+    lds_wait();  // this stage's LDS reads finish before the next step's DMA refills it
   };
 
   int n = 0;
@@ -396,12 +426,17 @@ decode_split_bf16_d128(AttnArgs a) {
     const float Mu = M == SOC_NEG_INF ? 0.f : M;
     const float Lt = mlx[0][l32][1] * fast_exp2(m0 - Mu) + mlx[1][l32][1] * fast_exp2(m1 - Mu) + fast_exp2(sink_l2 - Mu);
     const float wgt = Lt > 0.f ? fast_exp2(m_run - Mu) / Lt : 0.f;
-    float* xo = reinterpret_cast<float*>(vlds + NST * VSTAGE);  // wave 1's stages: 64 floats per lane
+    // wave 1's stages 0 and 1: 32 floats per lane each (O columns tb = 0, 1 and tb = 2, 3)
+    float* xo0 = reinterpret_cast<float*>(vst0 + VSTAGE);
+    float* xo1 = reinterpret_cast<float*>(vst1 + VSTAGE);
+    auto xo = [&](int idx) __attribute__((always_inline)) -> float& {
+      return idx < 32 ? xo0[idx * 64 + lane] : xo1[(idx - 32) * 64 + lane];
+    };
     if (wave == 1) {
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) xo[(tb * 16 + v) * 64 + lane] = oacc[tb][v] * wgt;
+        for (int v = 0; v < 16; ++v) xo(tb * 16 + v) = oacc[tb][v] * wgt;
     }
     __syncthreads();
     if (wave == 0 && row_ok) {
@@ -413,7 +448,7 @@ decode_split_bf16_d128(AttnArgs a) {
           bf16x4 w;
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            w[e] = (bf16_t)fmaf(oacc[tb][4 * g4 + e], wgt, xo[(tb * 16 + 4 * g4 + e) * 64 + lane]);
+            w[e] = (bf16_t)fmaf(oacc[tb][4 * g4 + e], wgt, xo(tb * 16 + 4 * g4 + e));
           *(bf16x4*)(orow + tb * 32 + 8 * g4 + 4 * hh) = w;
         }
     }

@@ -370,19 +370,30 @@ __global__ void __launch_bounds__(1024) dsa_topk_kernel(DsaArgs A) {
 // ---------------------------------------------------------------------------------------
 __device__ __forceinline__ int v_off(int row, int chunk) { return row * D + ((chunk ^ ((row & 3) << 2)) << 3); }
 
-__device__ __forceinline__ void wait_blocks(int blocks_after) {
-  static_assert(NST - 1 <= 3, "vmcnt holds at most 63 outstanding loads: 3 blocks of 16");
-  if (blocks_after >= 2)
-    asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
-  else if (blocks_after == 1)
-    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-  else
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+// Waits go through the s_waitcnt builtin: the compiler treats it as touching all memory (no
+// LDS access moves across it) and knows what it waited for, so it adds no drain of its own.
+// gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N <= 63, "vmcnt counts at most 63 loads");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+__device__ __forceinline__ void lds_wait() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
+
+static_assert(16 * (NST - 1) <= 63, "vmcnt holds at most 63 outstanding loads");
 
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) dsa_split_kernel(DsaArgs A) {
   const AttnArgs& a = A.at;
-  __shared__ __attribute__((aligned(1024))) bf16_t vlds[NST * VSTAGE];
+  // one LDS variable per V stage, so that the compiler can tell which stage a pending DMA
+  // writes (with one array it drains every load before each block's V reads)
+  static_assert(NST == 3, "one LDS variable per stage");
+  __shared__ __attribute__((aligned(1024))) bf16_t vst0[VSTAGE];
+  __shared__ __attribute__((aligned(1024))) bf16_t vst1[VSTAGE];
+  __shared__ __attribute__((aligned(1024))) bf16_t vst2[VSTAGE];
+  auto vstage = [&](auto stage_tag) __attribute__((always_inline)) -> bf16_t* {
+    constexpr int ST = decltype(stage_tag)::value;
+    return ST == 0 ? vst0 : ST == 1 ? vst1 : vst2;
+  };
   __shared__ int32_t ent[MAX_SPLIT];
 
   const int lane = threadIdx.x;
@@ -410,7 +421,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) ds
     u32x4 z = {0u, 0u, 0u, 0u};
     qf[ks] = row_ok ? *(const bf16x8*)(qp + 16 * ks + 8 * hh) : as_bf16x8(z);
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the list and q are in; only block loads are counted below
+  vm_wait<0>();  // the list and q are in; only block loads are counted below
   __syncthreads();
 
   const uint32_t row_bytes = (uint32_t)a.kv_st * 2u;
@@ -430,11 +441,16 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) ds
       kreg[ST][ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(krs, krow + hh * 16 + ks * 32, 0, 0));
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void_ptr)(vlds + ST * VSTAGE + i * 512), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void_ptr)(vstage(stage_tag) + i * 512), 16,
                                                (uint32_t)ent[n * KB + 4 * i + vr] * row_bytes + v_sw, 0, 0, 0);
   };
-  if (nblk > 0) issue(0, std::integral_constant<int, 0>{});
-  if (nblk > 1) issue(1, std::integral_constant<int, 1>{});
+  // Every step issues one block (past the last block it issues the last block again, into a
+  // stage already consumed), so exactly NST - 1 blocks are younger than the one a step
+  // consumes and one constant wait covers every step.
+  if (nblk > 0) {
+    issue(0, std::integral_constant<int, 0>{});
+    issue(min(1, nblk - 1), std::integral_constant<int, 1>{});
+  }
 
   f32x16 oacc[4];
 #pragma unroll
@@ -457,9 +473,12 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) ds
 
   auto step = [&](int n, auto stage_tag) __attribute__((always_inline)) {
     constexpr int ST = decltype(stage_tag)::value;
-    if (n + NST - 1 < nblk) issue(n + NST - 1, std::integral_constant<int, (ST + NST - 1) % NST>{});
-    wait_blocks(min(NST - 1, nblk - 1 - n));
-    const bf16_t* vt = vlds + ST * VSTAGE;
+    issue(min(n + NST - 1, nblk - 1), std::integral_constant<int, (ST + NST - 1) % NST>{});
+    // Block n's K registers and V stage have landed.  Loads into registers and LDS-DMA loads
+    // each retire in issue order but not in order with each other, so the wait allows only
+    // the 8 * (NST - 1) loads of one kind that were issued after block n's.
+    vm_wait<8 * (NST - 1)>();
+    const bf16_t* vt = vstage(stage_tag);
     const int js = ks0 + n * KB;  // list position of the block's first entry
 
     f32x16 sacc;
@@ -505,14 +524,18 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) ds
         const s16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         oacc[tb] = mfma32x32x16(__builtin_bit_cast(bf16x8, va), pb[kk], oacc[tb]);
       }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this stage's LDS reads finish before its refill
+    lds_wait();  // this stage's LDS reads finish before its refill
   };
 
-  for (int n = 0; n < nblk; n += NST) {
+  int n = 0;
+  for (; n + NST <= nblk; n += NST) {
     step(n, std::integral_constant<int, 0>{});
-    if (n + 1 < nblk) step(n + 1, std::integral_constant<int, 1>{});
-    if (n + 2 < nblk) step(n + 2, std::integral_constant<int, 2>{});
+    step(n + 1, std::integral_constant<int, 1>{});
+    step(n + 2, std::integral_constant<int, 2>{});
   }
+  if (n < nblk) step(n, std::integral_constant<int, 0>{});
+  if (n + 1 < nblk) step(n + 1, std::integral_constant<int, 1>{});
+  vm_wait<0>();  // the repeated last blocks land before the LDS is released
 
   // every split writes its partial, an empty one (max -inf, sum 0, O 0) included
   const float L = pair_sum(l_run);
