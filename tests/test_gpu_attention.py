@@ -93,6 +93,30 @@ def test_bf16_prefill_matches_oracle(case):
     assert err <= BF16_TOL, err
 
 
+# Windowed GQA on the grid that gives each XCD whole KV groups (batch x n_kv a multiple of 8):
+# the launch the window workload is timed in.  g = 4 stacks four heads over 32 rows, g = 2 two
+# heads over 64 rows; every element is compared.
+STACKED_CASES = [
+    # B, Hq, Hkv, Tq, Tk, offsets, window
+    (2, 16, 4, 700, 1300, [600, 37], 150),
+    (4, 8, 4, 333, 900, [0, 567, 200, 301], 150),
+    (1, 32, 8, 257, 2000, [1743], 1024),
+    (2, 16, 4, 64, 700, [636, 5], 7),
+]
+
+
+@pytest.mark.parametrize("case", STACKED_CASES)
+def test_bf16_window_gqa_stacked_heads_xcd_grouped(case):
+    B, Hq, Hkv, Tq, Tk, offs, W = case
+    announce(f"bf16 windowed GQA, stacked heads on the XCD-grouped grid {case}")
+    assert (B * Hkv) % 8 == 0 and (Hq // Hkv) % 2 == 0
+    w = synth.attention_inputs(B, Hq, Hkv, Tq, Tk, 128, torch.bfloat16, seed=Tq + W, with_sink=True, window=W,
+                               cache_off=offs)
+    o = run_prefill(w)
+    err = max_abs(o, oracle_of(w))
+    assert err <= BF16_TOL, err
+
+
 def test_bf16_prefill_strided_views():
     # q/k/v/o as views into larger buffers (head-major and token-major layouts)
     base = synth.normal((1, 300, 12, 128), 5, torch.bfloat16)  # [B, T, H, d] layout

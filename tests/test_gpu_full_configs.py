@@ -47,7 +47,9 @@ def test_window_sink_prefill_T32768_full_size():
     w = synth.window_sink_prefill(T=32768, W=1024)
     o = attn_prefill(w.q.cuda(), w.k.cuda(), w.v.cuda(), cache_off=w.cache_off.cuda(), window=1024,
                      sink=w.sink.cuda())
-    check_rows(o, w, sample_rows(32768, 16), [1, 30])
+    # every head: the workgroups stack 4 heads of a KV group, so each head position in the stack
+    # and each KV group is covered
+    check_rows(o, w, sample_rows(32768, 12), list(range(32)))
 
 
 def test_decode_and_chunk_B64_full_size():
@@ -62,10 +64,15 @@ def test_decode_and_chunk_B64_full_size():
     assert err <= BF16_TOL and bool(torch.isfinite(od).all())
     oc = attn_prefill(c.q_chunk.cuda(), k, v, cache_off=off)
     wc = c.prefill_chunk()
-    rows = [0, 1, 127, 128, 255, 256, 511]
-    ref = attend(wc.q, wc.k, wc.v, cache_off=wc.cache_off, rows=rows, heads=[5], batches=[0, 17, 63])
-    err = float(np.max(np.abs(host64(oc[[0, 17, 63]][:, [5]][:, :, rows]) - ref)))
-    announce(f"chunk 512 at cache offsets: max-abs err {err:.3e}")
+    # all 32 heads of 8 sequences (the shortest and longest caches among them) at the rows on
+    # either side of every 32-row wave block and 128-row workgroup edge
+    rows = [0, 1, 31, 32, 63, 64, 95, 96, 127, 128, 255, 256, 383, 384, 510, 511]
+    L = c.lengths.numpy()
+    seqs = sorted({int(np.argmin(L)), int(np.argmax(L)), 0, 9, 17, 30, 45, 63})
+    ref = attend(wc.q, wc.k, wc.v, cache_off=wc.cache_off, rows=rows, batches=seqs)
+    err = float(np.max(np.abs(host64(oc[seqs][:, :, rows]) - ref)))
+    announce(f"chunk 512 at cache offsets: max-abs err {err:.3e} over {len(seqs)} sequences x 32 heads x "
+             f"{len(rows)} rows")
     assert err <= BF16_TOL and bool(torch.isfinite(oc).all())
 
 
