@@ -132,6 +132,28 @@ int attn_decode(const attn_shape_t* shape, const void* q, attn_strides_t q_strid
                 void* workspace, size_t workspace_bytes, int32_t split_tokens, hipStream_t stream);
 
 /*
+ * attn_decode_noalloc -- attn_decode for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation, kernels and arguments as attn_decode, without the workspace
+ * arguments.  The per-split partials go to a scratch array the library holds in device
+ * memory, one per GPU it runs on, of attn_decode_noalloc_max_scratch_bytes() bytes
+ * (32 MiB), kept until the process ends.  Nothing is allocated or freed by the call.
+ *  - Shapes whose workspace (attn_decode_workspace_bytes) exceeds that size are rejected
+ *    with ATTN_E_WORKSPACE; use attn_decode with a caller workspace for those.
+ *  - All calls on one GPU share its array, which keeps the last call's contents (no part
+ *    of it needs to start at zero).  Calls that overlap on one GPU (concurrent streams or
+ *    threads) race on it: serialise them, e.g. on one stream.
+ *  - ATTN_DEBUG's host check of cache_off is not made (it copies to host memory).
+ */
+int attn_decode_noalloc(const attn_shape_t* shape, const void* q, attn_strides_t q_strides, const void* k,
+                        const void* v, attn_strides_t kv_strides, void* o, attn_strides_t o_strides,
+                        const int32_t* cache_off, int32_t window, const float* sink, float scale,
+                        int32_t split_tokens, hipStream_t stream);
+
+/* attn_decode_noalloc_max_scratch_bytes -- size of attn_decode_noalloc's per-GPU scratch. */
+size_t attn_decode_noalloc_max_scratch_bytes(void);
+
+/*
  * attn_ring_decode_workspace_bytes -- bytes of device workspace attn_ring_decode needs
  * (split_tokens <= 0 selects the default split).  Returns 0 for an invalid shape.
  */

@@ -5,6 +5,7 @@ The computation lives in hand-written HIP kernels behind the C ABI of
 
     attn_prefill(q, k, v, cache_off=None, window=0, sink=None, scale=None, block_list=None)
     attn_decode(q, k, v, cache_off=None, window=0, sink=None, scale=None, split_tokens=0)
+    attn_decode_noalloc(q, k, v, cache_off=None, window=0, sink=None, scale=None, split_tokens=0, out=None)
     attn_ring_decode(q, k_new, v_new, k_ring, v_ring, n_seen, sink=None, scale=None)
     attn_mla_decode(q_nope, q_rope, c_kv, k_rope, w_uk, w_uv, cache_off=None)
     attn_dsa_decode(q, k, v, qi, ki, wi, topk, cache_off=None, sink=None)
@@ -20,6 +21,8 @@ from .api import (  # noqa: F401
     attn_block_select,
     attn_block_select_workspace_bytes,
     attn_decode,
+    attn_decode_noalloc,
+    attn_decode_noalloc_max_scratch_bytes,
     attn_decode_workspace_bytes,
     attn_dsa_decode,
     attn_dsa_decode_workspace_bytes,

@@ -14,6 +14,8 @@ EXPORTS = (
     "attn_prefill",
     "attn_decode_workspace_bytes",
     "attn_decode",
+    "attn_decode_noalloc",
+    "attn_decode_noalloc_max_scratch_bytes",
     "attn_ring_decode_workspace_bytes",
     "attn_ring_decode",
     "attn_mla_decode_workspace_bytes",
@@ -63,6 +65,11 @@ def load() -> ctypes.CDLL:
     lib.attn_decode.argtypes = [POINTER(AttnShape), P, AttnStrides, P, P, AttnStrides, P, AttnStrides,
                                 P, c_int32, P, c_float, P, c_size_t, c_int32, P]
     lib.attn_decode.restype = c_int
+    lib.attn_decode_noalloc.argtypes = [POINTER(AttnShape), P, AttnStrides, P, P, AttnStrides, P, AttnStrides,
+                                        P, c_int32, P, c_float, c_int32, P]
+    lib.attn_decode_noalloc.restype = c_int
+    lib.attn_decode_noalloc_max_scratch_bytes.argtypes = []
+    lib.attn_decode_noalloc_max_scratch_bytes.restype = c_size_t
     lib.attn_ring_decode_workspace_bytes.argtypes = [POINTER(AttnShape), c_int32]
     lib.attn_ring_decode_workspace_bytes.restype = c_size_t
     lib.attn_ring_decode.argtypes = [POINTER(AttnShape), P, AttnStrides, P, P, AttnStrides, P, P, AttnStrides,

@@ -129,6 +129,23 @@ def attn_decode(q, k, v, cache_off=None, window=0, sink=None, scale=None, split_
     return o
 
 
+def attn_decode_noalloc_max_scratch_bytes() -> int:
+    return int(_lib.load().attn_decode_noalloc_max_scratch_bytes())
+
+
+def attn_decode_noalloc(q, k, v, cache_off=None, window=0, sink=None, scale=None, split_tokens=0, out=None):
+    """attn_decode without a workspace: the library's per-GPU scratch holds the partials (see
+    attn_decode_noalloc in include/soc_attn.h).  Pass ``out`` to allocate nothing at all."""
+    _common(q, k, v, cache_off, sink)
+    o = _out(q, out)
+    lib = _lib.load()
+    rc = lib.attn_decode_noalloc(_shape(q, k), q.data_ptr(), _strides(q), k.data_ptr(), v.data_ptr(), _strides(k),
+                                 o.data_ptr(), _strides(o), _ptr(cache_off), int(window), _ptr(sink),
+                                 float(scale or 0.0), int(split_tokens), _stream())
+    _check(rc)
+    return o
+
+
 def attn_ring_decode_workspace_bytes(q, k_ring, split_tokens=0) -> int:
     return int(_lib.load().attn_ring_decode_workspace_bytes(_shape(q, k_ring), int(split_tokens)))
 

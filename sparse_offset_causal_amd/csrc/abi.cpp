@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -310,10 +311,42 @@ size_t attn_decode_workspace_bytes(const attn_shape_t* shape, int32_t split_toke
   return round_up(rows * nsplit * (shape->head_dim + 2) * sizeof(float), 256);
 }
 
-int attn_decode(const attn_shape_t* shape, const void* q, attn_strides_t q_strides, const void* k, const void* v,
+}  // extern "C"
+
+namespace {
+
+// Scratch of attn_decode_noalloc: the decode workspace (per-split partials) for callers that
+// cannot allocate.  Each device the library runs on holds its own copy of the array until
+// the process ends; host code reaches it only through the address hipGetSymbolAddress
+// returns for the current device (the array's name is a host-side stand-in).
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Address of the current device's scratch array, looked up once per device.
+int noalloc_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "attn_decode_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(ATTN_E_UNSUPPORTED, "attn_decode_noalloc: device index above 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return hip_fail(e, "attn_decode_noalloc: hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ATTN_OK;
+}
+
+int decode_impl(const attn_shape_t* shape, const void* q, attn_strides_t q_strides, const void* k, const void* v,
                 attn_strides_t kv_strides, void* o, attn_strides_t o_strides, const int32_t* cache_off,
                 int32_t window, const float* sink, float scale, void* workspace, size_t workspace_bytes,
-                int32_t split_tokens, hipStream_t stream) {
+                int32_t split_tokens, hipStream_t stream, bool noalloc) {
   int rc = check_shape(shape);
   if (rc) return rc;
   if ((rc = check_attn_dtype(shape))) return rc;
@@ -329,13 +362,22 @@ int attn_decode(const attn_shape_t* shape, const void* q, attn_strides_t q_strid
   const int split = split_tokens > 0 ? split_tokens : default_split(shape);
   const int64_t nsplit = (shape->tk + split - 1) / split;
   const size_t need = attn_decode_workspace_bytes(shape, split);
+  if (noalloc) {
+    if (need > kNoAllocScratchBytes)
+      return fail(ATTN_E_WORKSPACE, "attn_decode_noalloc: this shape needs " + std::to_string(need) +
+                                        " bytes of scratch, above the library's fixed " +
+                                        std::to_string(kNoAllocScratchBytes) + " (use attn_decode with a workspace)");
+    if ((rc = noalloc_scratch(&workspace))) return rc;
+    workspace_bytes = kNoAllocScratchBytes;
+  }
   if (!workspace) return fail(ATTN_E_WORKSPACE, "workspace is NULL");
   if (!aligned16(workspace)) return fail(ATTN_E_WORKSPACE, "workspace must be 16-byte aligned");
   if (workspace_bytes < need)
     return fail(ATTN_E_WORKSPACE, "workspace too small: need " + std::to_string(need) + " bytes");
   if ((int64_t)shape->batch * shape->n_heads * shape->tq * nsplit >= (int64_t)1 << 31)
     return fail(ATTN_E_INVAL, "problem too large for one grid");
-  if ((rc = check_offsets_debug(shape, cache_off, stream))) return rc;
+  // (the ATTN_DEBUG offset check copies the offsets into host memory: not done without allocation)
+  if (!noalloc && (rc = check_offsets_debug(shape, cache_off, stream))) return rc;
 
   soc::AttnArgs a = make_args(shape, q, q_strides, k, v, kv_strides, o, o_strides, cache_off, window, sink, scale);
   a.part = static_cast<float*>(workspace);
@@ -348,6 +390,28 @@ int attn_decode(const attn_shape_t* shape, const void* q, attn_strides_t q_strid
   if (e != hipSuccess) return hip_fail(e, "attn_decode split launch");
   e = soc::launch_decode_merge(a, shape->dtype == ATTN_BF16, stream);
   return finish(e, stream, "attn_decode merge launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_decode(const attn_shape_t* shape, const void* q, attn_strides_t q_strides, const void* k, const void* v,
+                attn_strides_t kv_strides, void* o, attn_strides_t o_strides, const int32_t* cache_off,
+                int32_t window, const float* sink, float scale, void* workspace, size_t workspace_bytes,
+                int32_t split_tokens, hipStream_t stream) {
+  return decode_impl(shape, q, q_strides, k, v, kv_strides, o, o_strides, cache_off, window, sink, scale, workspace,
+                     workspace_bytes, split_tokens, stream, false);
+}
+
+size_t attn_decode_noalloc_max_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+int attn_decode_noalloc(const attn_shape_t* shape, const void* q, attn_strides_t q_strides, const void* k,
+                        const void* v, attn_strides_t kv_strides, void* o, attn_strides_t o_strides,
+                        const int32_t* cache_off, int32_t window, const float* sink, float scale,
+                        int32_t split_tokens, hipStream_t stream) {
+  return decode_impl(shape, q, q_strides, k, v, kv_strides, o, o_strides, cache_off, window, sink, scale, nullptr, 0,
+                     split_tokens, stream, true);
 }
 
 size_t attn_ring_decode_workspace_bytes(const attn_shape_t* shape, int32_t split_tokens) {
