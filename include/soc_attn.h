@@ -86,26 +86,35 @@ typedef struct {
  * prefill or decode) against the cache.
  *
  *  q          [batch, n_heads, tq, head_dim]   (dtype)
- *  k, v       [batch, n_kv, tk, head_dim]      (dtype), strides kv_strides
+ *  k, v       [batch, n_kv, tk, head_dim]      (dtype), strides kv_strides (bf16: the
+ *             token stride must be nonzero, else ATTN_E_UNSUPPORTED)
  *  o          [batch, n_heads, tq, head_dim]   output (dtype), written for every row
  *  cache_off  device int32 [batch], or NULL (off_b = tk - tq)
  *  window     <= 0: no window; W > 0 keeps keys pos-W < j <= pos.  Key tiles entirely
  *             outside the window or beyond pos are never read.
  *  sink       device float32 [n_heads] or NULL (a -inf entry behaves as no sink)
  *  scale      <= 0 means 1/sqrt(head_dim)
- *  block_list NULL for dense, or device int32 [batch, n_heads, nQB, 1 + nKB] with
- *             nQB = ceil(tq / block_size), nKB = ceil(tk / block_size): entry 0 of each
- *             (b, h, qb) row is the count n of kept key blocks, entries 1..n the kept key
- *             block indices in ascending order (as written by attn_block_select).  Query
- *             block qb covers rows [qb*bs, (qb+1)*bs) of the tq block; key block kb covers
- *             absolute keys [kb*bs, (kb+1)*bs).  Unlisted key blocks are never read
+ *  block_mask NULL, or device uint8 [batch, n_heads, nQB, nKB] with nQB = ceil(tq /
+ *             block_size), nKB = ceil(tk / block_size): a nonzero entry keeps key block kb
+ *             for query block qb of head h (the attend(q, k, v, mask, sink) mask of
+ *             sotaaz.com/post/attention-in-code, "the one function every design uses", at
+ *             block granularity).  Query block qb covers rows [qb*bs, (qb+1)*bs) of the tq
+ *             block; key block kb covers absolute keys [kb*bs, (kb+1)*bs).  The causal and
+ *             window rules still apply inside kept blocks; unkept key blocks are never read
  *             (patty.io RBS-Attention review, section on regular block-sparse execution).
- *  block_size ignored when block_list is NULL; bf16 path requires 128.
+ *             The kernel walks each mask row itself: no workspace is needed.
+ *  block_list NULL, or the same selection as kept-block lists: device int32 [batch, n_heads,
+ *             nQB, 1 + nKB], entry 0 of each (b, h, qb) row the count n of kept key blocks,
+ *             entries 1..n the kept key block indices in ascending order (as written by
+ *             attn_block_select).  At most one of block_mask and block_list may be non-NULL
+ *             (both: ATTN_E_INVAL); with neither the prefill is dense.
+ *  block_size ignored when both are NULL; bf16 path requires 128.
  */
 int attn_prefill(const attn_shape_t* shape, const void* q, attn_strides_t q_strides, const void* k,
                  const void* v, attn_strides_t kv_strides, void* o, attn_strides_t o_strides,
                  const int32_t* cache_off, int32_t window, const float* sink, float scale,
-                 const int32_t* block_list, int32_t block_size, hipStream_t stream);
+                 const uint8_t* block_mask, const int32_t* block_list, int32_t block_size,
+                 hipStream_t stream);
 
 /*
  * attn_decode_workspace_bytes -- bytes of device workspace attn_decode needs for this

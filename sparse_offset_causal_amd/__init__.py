@@ -3,7 +3,7 @@
 The computation lives in hand-written HIP kernels behind the C ABI of
 ``include/soc_attn.h`` (``libsoc_attn.so``); this package is the thin binding:
 
-    attn_prefill(q, k, v, cache_off=None, window=0, sink=None, scale=None, block_list=None)
+    attn_prefill(q, k, v, cache_off=None, window=0, sink=None, scale=None, block_mask=None, block_list=None)
     attn_decode(q, k, v, cache_off=None, window=0, sink=None, scale=None, split_tokens=0)
     attn_decode_noalloc(q, k, v, cache_off=None, window=0, sink=None, scale=None, split_tokens=0, out=None)
     attn_ring_decode(q, k_new, v_new, k_ring, v_ring, n_seen, sink=None, scale=None)

@@ -58,7 +58,7 @@ def load() -> ctypes.CDLL:
     lib = ctypes.CDLL(LIB_PATH)
     P = c_void_p
     lib.attn_prefill.argtypes = [POINTER(AttnShape), P, AttnStrides, P, P, AttnStrides, P, AttnStrides,
-                                 P, c_int32, P, c_float, P, c_int32, P]
+                                 P, c_int32, P, c_float, P, P, c_int32, P]
     lib.attn_prefill.restype = c_int
     lib.attn_decode_workspace_bytes.argtypes = [POINTER(AttnShape), c_int32]
     lib.attn_decode_workspace_bytes.restype = c_size_t

@@ -88,20 +88,27 @@ def _out(q, out):
     return out
 
 
-def attn_prefill(q, k, v, cache_off=None, window=0, sink=None, scale=None, block_list=None,
+def attn_prefill(q, k, v, cache_off=None, window=0, sink=None, scale=None, block_mask=None, block_list=None,
                  block_size=128, out=None):
     """Offset-causal attention of q [B,Hq,Tq,d] against the cache k, v [B,Hkv,Tk,d] (see attn_prefill in
-    include/soc_attn.h).  block_list: int32 [B, Hq, ceil(Tq/bs), 1 + ceil(Tk/bs)] from attn_block_select."""
+    include/soc_attn.h).  block_mask: uint8 [B, Hq, ceil(Tq/bs), ceil(Tk/bs)], nonzero = kept; or
+    block_list: int32 [B, Hq, ceil(Tq/bs), 1 + ceil(Tk/bs)] from attn_block_select."""
     _common(q, k, v, cache_off, sink)
     o = _out(q, out)
     if block_list is not None and (block_list.dtype != torch.int32 or not block_list.is_cuda or
                                    not block_list.is_contiguous()):
         raise ValueError("block_list must be a contiguous int32 GPU tensor")
+    if block_mask is not None:
+        nqb, nkb = -(-q.shape[2] // block_size), -(-k.shape[2] // block_size)
+        if (block_mask.dtype != torch.uint8 or not block_mask.is_cuda or not block_mask.is_contiguous() or
+                tuple(block_mask.shape) != (q.shape[0], q.shape[1], nqb, nkb)):
+            raise ValueError(f"block_mask must be a contiguous uint8 GPU tensor of shape "
+                             f"{(q.shape[0], q.shape[1], nqb, nkb)}")
     lib = _lib.load()
     shape = _shape(q, k)
     rc = lib.attn_prefill(shape, q.data_ptr(), _strides(q), k.data_ptr(), v.data_ptr(), _strides(k),
                           o.data_ptr(), _strides(o), _ptr(cache_off), int(window), _ptr(sink),
-                          float(scale or 0.0), _ptr(block_list), int(block_size), _stream())
+                          float(scale or 0.0), _ptr(block_mask), _ptr(block_list), int(block_size), _stream())
     _check(rc)
     return o
 

@@ -69,6 +69,9 @@ int check_tensors(const attn_shape_t* s, const void* q, attn_strides_t qs, const
     return fail(ATTN_E_INVAL, "q, k, v and o must be 16-byte aligned");
   if (!strides_ok(qs, esz) || !strides_ok(kvs, esz) || !strides_ok(os, esz))
     return fail(ATTN_E_INVAL, "strides must be non-negative multiples of 16 bytes (in elements)");
+  // the bf16 kernels address K/V through buffer ranges of (rows x token stride) bytes
+  if (s->dtype == ATTN_BF16 && kvs.t == 0)
+    return fail(ATTN_E_UNSUPPORTED, "bf16 k/v need a nonzero token stride (one row per token)");
   return ATTN_OK;
 }
 
@@ -271,8 +274,8 @@ const char* attn_last_error(void) { return g_err.c_str(); }
 
 int attn_prefill(const attn_shape_t* shape, const void* q, attn_strides_t q_strides, const void* k, const void* v,
                  attn_strides_t kv_strides, void* o, attn_strides_t o_strides, const int32_t* cache_off,
-                 int32_t window, const float* sink, float scale, const int32_t* block_list, int32_t block_size,
-                 hipStream_t stream) {
+                 int32_t window, const float* sink, float scale, const uint8_t* block_mask,
+                 const int32_t* block_list, int32_t block_size, hipStream_t stream) {
   int rc = check_shape(shape);
   if (rc) return rc;
   if ((rc = check_attn_dtype(shape))) return rc;
@@ -281,8 +284,9 @@ int attn_prefill(const attn_shape_t* shape, const void* q, attn_strides_t q_stri
     return ATTN_OK;
   }
   if ((rc = check_tensors(shape, q, q_strides, k, v, kv_strides, o, o_strides))) return rc;
-  if (block_list) {
-    if (block_size < 1) return fail(ATTN_E_INVAL, "block_size must be >= 1 with a block list");
+  if (block_mask && block_list) return fail(ATTN_E_INVAL, "pass a block mask or a block list, not both");
+  if (block_list || block_mask) {
+    if (block_size < 1) return fail(ATTN_E_INVAL, "block_size must be >= 1 with a block mask or list");
     if (shape->dtype == ATTN_BF16 && block_size != 128)
       return fail(ATTN_E_UNSUPPORTED, "the bf16 block-sparse prefill needs block_size 128");
   }
@@ -293,11 +297,13 @@ int attn_prefill(const attn_shape_t* shape, const void* q, attn_strides_t q_stri
   if ((rc = check_offsets_debug(shape, cache_off, stream))) return rc;
 
   soc::AttnArgs a = make_args(shape, q, q_strides, k, v, kv_strides, o, o_strides, cache_off, window, sink, scale);
-  if (block_list) {
+  if (block_list || block_mask) {
     a.block_list = block_list;
+    a.block_mask = block_mask;
     a.block_size = block_size;
     a.n_qb = (shape->tq + block_size - 1) / block_size;
-    a.list_stride = 1 + (shape->tk + block_size - 1) / block_size;
+    a.mask_stride = (shape->tk + block_size - 1) / block_size;
+    a.list_stride = 1 + a.mask_stride;
   }
   const hipError_t e = shape->dtype == ATTN_BF16 ? soc::launch_prefill_bf16(a, stream) : soc::launch_prefill_f32(a, stream);
   return finish(e, stream, "attn_prefill launch");

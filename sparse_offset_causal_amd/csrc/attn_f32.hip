@@ -78,13 +78,20 @@ __global__ void __launch_bounds__(64) prefill_f32_kernel(AttnArgs a) {
     st.init(a.sink[h] * kLog2e, 1.f);
   else
     st.init(SOC_NEG_INF, 0.f);
-  if (SPARSE) {
+  if (SPARSE && a.block_list) {
     const int32_t* lst = a.block_list + ((int64_t)(b * a.Hq + h) * a.n_qb + r / a.block_size) * a.list_stride;
     const int cnt = lst[0];
     for (int e = 0; e < cnt; ++e) {
       const int kb = lst[1 + e];
       const int j0 = max(lo, kb * a.block_size), j1 = min(pos, kb * a.block_size + a.block_size - 1);
       if (j0 <= j1) st.run(q, kp, vp, a.kv_st, j0, j1, a.scale_log2);
+    }
+  } else if (SPARSE) {  // block mask: the key blocks of the row's range that the mask marks
+    const uint8_t* mrow = a.block_mask + ((int64_t)(b * a.Hq + h) * a.n_qb + r / a.block_size) * a.mask_stride;
+    for (int kb = lo / a.block_size; kb <= pos / a.block_size; ++kb) {
+      if (!mrow[kb]) continue;
+      const int j0 = max(lo, kb * a.block_size), j1 = min(pos, kb * a.block_size + a.block_size - 1);
+      st.run(q, kp, vp, a.kv_st, j0, j1, a.scale_log2);
     }
   } else {
     st.run(q, kp, vp, a.kv_st, lo, pos, a.scale_log2);
@@ -133,7 +140,7 @@ template <int D>
 hipError_t launch_prefill_f32_d(const AttnArgs& a, hipStream_t s) {
   const int64_t total = (int64_t)a.B * a.Hq * a.tq;
   const unsigned grid = (unsigned)((total + 63) / 64);
-  if (a.block_list)
+  if (a.block_list || a.block_mask)
     hipLaunchKernelGGL((prefill_f32_kernel<D, true>), dim3(grid), dim3(64), 0, s, a);
   else
     hipLaunchKernelGGL((prefill_f32_kernel<D, false>), dim3(grid), dim3(64), 0, s, a);

@@ -23,9 +23,10 @@ struct AttnArgs {
   int32_t window;            // <= 0: none
   const float* sink;         // device [Hq] or null
   float scale_log2;          // softmax scale * log2(e)
-  // block-sparse prefill
+  // block-sparse prefill: a kept-block list or a block mask (at most one of them)
   const int32_t* block_list;  // device [B, Hq, n_qb, list_stride] or null
-  int32_t block_size, n_qb, list_stride;
+  const uint8_t* block_mask;  // device [B, Hq, n_qb, mask_stride] or null
+  int32_t block_size, n_qb, list_stride, mask_stride;
   // split-KV decode
   float* part;     // workspace: partial sums, [B*Hq*tq][nsplit][d] floats, then [..][nsplit][2]
   int32_t nsplit;  // splits per sequence (capacity)

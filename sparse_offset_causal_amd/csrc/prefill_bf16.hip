@@ -103,7 +103,7 @@ __device__ __forceinline__ void map_block(int bid, const AttnArgs& a, int n_rg, 
 // rows of one head (measured 1 % faster that way, the window 2 % slower); block-sparse mode
 // stacks rows only (its lists differ by head and are per 128-row block).
 __host__ __device__ inline int heads_per_workgroup(const AttnArgs& a) {
-  if (a.block_list || a.window <= 0) return 1;
+  if (a.block_list || a.block_mask || a.window <= 0) return 1;
   return (a.g & 3) == 0 ? 4 : (a.g & 1) == 0 ? 2 : 1;
 }
 
@@ -113,7 +113,11 @@ __device__ __forceinline__ int v_off(int row, int chunk) { return row * D + ((ch
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-template <bool SPARSE, bool HSTACK>
+// Which key blocks a workgroup walks: all in its range, those of a kept-block list, or those
+// a block mask marks.
+enum SparseMode { kDense = 0, kList = 1, kMask = 2 };
+
+template <int MODE, bool HSTACK>
 __global__ void __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2)))
 prefill_bf16_d128(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) bf16_t lds[2 * BUF_ELEMS];
@@ -152,11 +156,20 @@ prefill_bf16_d128(AttnArgs a) {
   const bf16_t* kp = (const bf16_t*)a.k + b * a.kv_sb + kvh * a.kv_sh;
   const bf16_t* vp = (const bf16_t*)a.v + b * a.kv_sb + kvh * a.kv_sh;
 
-  // Tile sequence: dense = t_lo .. t_hi-1; sparse = the two 64-key halves of each listed
-  // 128-key block, restricted to [t_lo, t_hi) (a contiguous run, the list is ascending).
+  // Tile sequence: dense = t_lo .. t_hi-1; sparse = the two 64-key halves of each listed (or
+  // marked) 128-key block, restricted to [t_lo, t_hi) (a contiguous run, in ascending order).
   const int32_t* lst = nullptr;
+  const uint8_t* mrow = nullptr;
   int n0 = 0, n1 = 0;
-  if (SPARSE) {
+  const int kb_lo = t_lo >> 1, kb_hi = (t_hi - 1) >> 1;  // key blocks holding tiles of the range
+  // Mask rows are read 64 key blocks at a time: lane j reads block c + j (blocks outside
+  // [kb_lo, kb_hi] count as not kept) and a ballot gives the wave-uniform set.
+  auto mask_bits = [&](int c) __attribute__((always_inline)) -> uint64_t {
+    const int kb = c + lane;
+    const bool kept = kb >= kb_lo && kb <= kb_hi && mrow[kb] != 0;
+    return __builtin_amdgcn_ballot_w64(kept);
+  };
+  if (MODE == kList) {
     lst = a.block_list + ((int64_t)(b * a.Hq + h) * a.n_qb + rg) * a.list_stride;  // rows of block rg
     const int cnt = lst[0];
     n1 = 2 * cnt;
@@ -164,6 +177,17 @@ prefill_bf16_d128(AttnArgs a) {
     int e = n0;
     while (e < n1 && 2 * lst[1 + (e >> 1)] + (e & 1) < t_hi) ++e;
     n1 = e;
+  } else if (MODE == kMask) {
+    mrow = a.block_mask + ((int64_t)(b * a.Hq + h) * a.n_qb + rg) * a.mask_stride;
+    if (t_lo < t_hi) {
+      int kept = 0;
+      for (int c = kb_lo; c <= kb_hi; c += 64) kept += __builtin_popcountll(mask_bits(c));
+      // each kept block holds two tiles, less a half below t_lo or at t_hi
+      n1 = 2 * kept;
+      if ((t_lo & 1) && mrow[kb_lo] != 0) --n1;
+      if ((t_hi & 1) && mrow[kb_hi] != 0) --n1;
+      n1 = __builtin_amdgcn_readfirstlane(n1);
+    }
   } else {
     n1 = max(0, t_hi - t_lo);
   }
@@ -171,8 +195,30 @@ prefill_bf16_d128(AttnArgs a) {
   // lchunk + j), so a tile's index is a lane read rather than a memory round trip that would
   // sit between a tile's start and its successor's DMA.
   int lchunk = -64, lreg = 0;
+  // Mask mode walks its row in order: mc is the chunk of 64 blocks being read, mbits its kept
+  // blocks not yet taken, mkb the block whose upper half comes next when modd is set.
+  int mc = kb_lo - 64, mkb = 0;
+  uint64_t mbits = 0;
+  bool modd = false;
   auto tile_of = [&](int n) __attribute__((always_inline)) -> int {
-    if (!SPARSE) return t_lo + n;
+    if (MODE == kDense) return t_lo + n;
+    if (MODE == kMask) {  // the next tile of the sequence (tiles are asked for in order)
+      for (;;) {
+        if (modd) {
+          modd = false;
+          if (2 * mkb + 1 < t_hi) return 2 * mkb + 1;
+          continue;
+        }
+        while (mbits == 0) {  // ends: the count says a kept block is left
+          mc += 64;
+          mbits = mask_bits(mc);
+        }
+        mkb = mc + __builtin_ctzll(mbits);
+        mbits &= mbits - 1;
+        modd = true;
+        if (2 * mkb >= t_lo) return 2 * mkb;
+      }
+    }
     const int e = n >> 1;
     if ((e & ~63) != lchunk) {  // uniform; once per 64 list entries
       lchunk = e & ~63;
@@ -208,7 +254,9 @@ prefill_bf16_d128(AttnArgs a) {
     }
   };
 
-  if (n0 < n1) issue_tile(tile_of(n0), 0);
+  // the tile of step n + 1, found (and its loads issued) at the start of step n
+  int t_next = n0 < n1 ? tile_of(n0) : 0;
+  if (n0 < n1) issue_tile(t_next, 0);
 
   bf16x8 qf[8];
 #pragma unroll
@@ -339,8 +387,11 @@ prefill_bf16_d128(AttnArgs a) {
 
   auto tile_step = [&](int n, auto buf_tag) __attribute__((always_inline)) {
     constexpr int BUF = decltype(buf_tag)::value;
-    const int t = tile_of(n);
-    if (n + 1 < n1) issue_tile(tile_of(n + 1), BUF ^ 1);
+    const int t = t_next;
+    if (n + 1 < n1) {
+      t_next = tile_of(n + 1);
+      issue_tile(t_next, BUF ^ 1);
+    }
     const bf16_t* kt = lds + BUF * BUF_ELEMS;
     const bf16_t* vt = kt + TILE_ELEMS;
 
@@ -387,11 +438,13 @@ hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t s) {
   const int64_t grid = (int64_t)n_rg * a.B * (a.Hq / gs);
   if (grid == 0) return hipSuccess;
   if (a.block_list)
-    hipLaunchKernelGGL((prefill_bf16_d128<true, false>), dim3((unsigned)grid), dim3(NTHR), 0, s, a);
+    hipLaunchKernelGGL((prefill_bf16_d128<kList, false>), dim3((unsigned)grid), dim3(NTHR), 0, s, a);
+  else if (a.block_mask)
+    hipLaunchKernelGGL((prefill_bf16_d128<kMask, false>), dim3((unsigned)grid), dim3(NTHR), 0, s, a);
   else if (gs > 1)
-    hipLaunchKernelGGL((prefill_bf16_d128<false, true>), dim3((unsigned)grid), dim3(NTHR), 0, s, a);
+    hipLaunchKernelGGL((prefill_bf16_d128<kDense, true>), dim3((unsigned)grid), dim3(NTHR), 0, s, a);
   else
-    hipLaunchKernelGGL((prefill_bf16_d128<false, false>), dim3((unsigned)grid), dim3(NTHR), 0, s, a);
+    hipLaunchKernelGGL((prefill_bf16_d128<kDense, false>), dim3((unsigned)grid), dim3(NTHR), 0, s, a);
   return hipGetLastError();
 }
 

@@ -50,16 +50,17 @@ def st(d=128, t=None, tk=64, h=8):
 
 
 def prefill(lib, shape, q=FAKE, k=FAKE, v=FAKE, o=FAKE, qs=None, kvs=None, os_=None, window=0, block_list=None,
-            block_size=128):
+            block_size=128, block_mask=None):
     qs = qs or st()
     kvs = kvs or st()
     os_ = os_ or st()
-    return lib.attn_prefill(ctypes.byref(shape), q, qs, k, v, kvs, o, os_, None, window, None, 0.0, block_list,
-                            block_size, None)
+    return lib.attn_prefill(ctypes.byref(shape), q, qs, k, v, kvs, o, os_, None, window, None, 0.0, block_mask,
+                            block_list, block_size, None)
 
 
 def test_invalid_shapes(lib):
-    assert lib.attn_prefill(None, FAKE, st(), FAKE, FAKE, st(), FAKE, st(), None, 0, None, 0.0, None, 0, None) == ATTN_E_INVAL
+    assert lib.attn_prefill(None, FAKE, st(), FAKE, FAKE, st(), FAKE, st(), None, 0, None, 0.0, None, None, 0,
+                            None) == ATTN_E_INVAL
     assert prefill(lib, S(h=6, kv=4)) == ATTN_E_INVAL
     assert "multiple of n_kv" in _lib.last_error()
     assert prefill(lib, S(tq=65, tk=64)) == ATTN_E_INVAL
@@ -73,6 +74,9 @@ def test_unsupported_combinations(lib):
     assert prefill(lib, S(d=48, dt=ATTN_F32)) == ATTN_E_UNSUPPORTED
     assert prefill(lib, S(), block_list=FAKE, block_size=64) == ATTN_E_UNSUPPORTED
     assert prefill(lib, S(), block_list=FAKE, block_size=0) == ATTN_E_INVAL
+    assert prefill(lib, S(), block_mask=FAKE, block_size=64) == ATTN_E_UNSUPPORTED
+    assert prefill(lib, S(), block_mask=FAKE, block_list=FAKE) == ATTN_E_INVAL
+    assert "not both" in _lib.last_error()
     shape = AttnShape(1, 32, 4, 128, 8, 64, ATTN_BF16)  # 8 query heads per KV head x 8 rows = 64 > 32
     ws = lib.attn_decode_workspace_bytes(ctypes.byref(shape), 0)
     rc = lib.attn_decode(ctypes.byref(shape), FAKE, st(h=32), FAKE, FAKE, st(h=4), FAKE, st(h=32), None, 0, None,
@@ -86,6 +90,19 @@ def test_null_and_misaligned_pointers(lib):
     assert prefill(lib, S(), k=FAKE + 2) == ATTN_E_INVAL
     assert "16-byte" in _lib.last_error()
     assert prefill(lib, S(), qs=AttnStrides(8192, 1024, 130)) == ATTN_E_INVAL
+
+
+def test_bf16_zero_token_stride_is_rejected(lib):
+    # the bf16 kernels address K/V through buffer ranges of rows x token stride bytes: a zero
+    # stride (one row broadcast over the tokens) would read zeros, so it is refused
+    assert prefill(lib, S(), kvs=AttnStrides(2 * 64 * 128, 64 * 128, 0)) == ATTN_E_UNSUPPORTED
+    assert "token stride" in _lib.last_error()
+    shape = S(tq=1, tk=1024)
+    need = lib.attn_ring_decode_workspace_bytes(ctypes.byref(shape), 256)
+    rc = lib.attn_ring_decode(ctypes.byref(shape), FAKE, st(tk=1), FAKE, FAKE, st(tk=1, h=2), FAKE, FAKE,
+                              AttnStrides(2 * 1024 * 128, 1024 * 128, 0), FAKE, st(tk=1), FAKE, None, 0.0, FAKE, need,
+                              256, None)
+    assert rc == ATTN_E_UNSUPPORTED
 
 
 def test_zero_sized_calls_are_noops(lib):

@@ -196,6 +196,42 @@ def test_bf16_block_list_random_mask_matches_oracle():
     assert torch.count_nonzero(o[0, 0, 128:256]) == 0
 
 
+@pytest.mark.parametrize("window,with_sink", [(0, False), (150, True), (333, False)])
+def test_bf16_block_mask_matches_block_list_and_oracle(window, with_sink):
+    """The block mask walked in the kernel selects the same tiles as its kept-block list (so the
+    two outputs are bitwise equal) and matches the oracle.  The mask marks future and
+    out-of-window blocks too (the causal and window rules still apply inside kept blocks) and
+    leaves one query block empty; offsets put the window edge and the last row mid-block."""
+    announce(f"bf16 block mask window={window} sink={with_sink}")
+    B, Hq, Hkv, Tq, Tk = 2, 8, 2, 500, 1300
+    offs = [800, 77]
+    w = synth.attention_inputs(B, Hq, Hkv, Tq, Tk, 128, torch.bfloat16, seed=31 + window, with_sink=with_sink,
+                               window=window, cache_off=offs)
+    g = torch.Generator().manual_seed(32 + window)
+    mask = (torch.rand((B, Hq, 4, 11), generator=g) < 0.45).to(torch.uint8)
+    mask[1, 3, 2] = 0
+    mask[0, 5] = 1
+    md = mask.cuda()
+    o_mask = run_prefill(w, block_mask=md, block_size=128)
+    o_list = run_prefill(w, block_list=attn_block_list_from_mask(md), block_size=128)
+    assert torch.equal(o_mask, o_list)
+    ref = oracle_of(w, block_mask=mask.numpy(), block_size=128)
+    assert max_abs(o_mask, ref) <= BF16_TOL
+    if not with_sink:
+        assert torch.count_nonzero(o_mask[1, 3, 256:384]) == 0
+    ones = torch.ones_like(md)
+    assert torch.equal(run_prefill(w, block_mask=ones, block_size=128), run_prefill(w))
+
+
+def test_f32_block_mask_matches_oracle():
+    w = synth.attention_inputs(2, 4, 2, 70, 130, 32, torch.float32, seed=33, with_sink=True, window=50,
+                               cache_off=[60, 10])
+    g = torch.Generator().manual_seed(34)
+    mask = (torch.rand((2, 4, 5, 9), generator=g) < 0.5).to(torch.uint8)
+    o = run_prefill(w, block_mask=mask.cuda(), block_size=16)
+    assert max_abs(o, oracle_of(w, block_mask=mask.numpy(), block_size=16)) <= F32_TOL
+
+
 # ---------------------------------------------------------------- bf16 decode
 @pytest.mark.parametrize("tq", [1, 2, 8])
 @pytest.mark.parametrize("split", [0, 256, 1000])
