@@ -236,7 +236,7 @@ MlaLayout mla_layout(const attn_mla_shape_t* s, int32_t split_tokens) {
 }
 
 struct DsaLayout {
-  size_t part, scores, list, count, total;
+  size_t part, scores, ebound, s64, band, list, count, total;
   int split, nsplit;
 };
 
@@ -258,6 +258,12 @@ DsaLayout dsa_layout(const attn_shape_t* s, int topk, int32_t split_tokens) {
   off = round_up(off + rows * L.nsplit * (s->head_dim + 2) * sizeof(float), 256);
   L.scores = off;
   off = round_up(off + qrows * (size_t)s->tk * sizeof(float), 256);
+  L.ebound = off;
+  off = round_up(off + qrows * (size_t)s->tk * sizeof(float), 256);
+  L.s64 = off;
+  off = round_up(off + qrows * (size_t)s->tk * sizeof(double), 256);
+  L.band = off;
+  off = round_up(off + qrows * (size_t)s->tk * sizeof(int32_t), 256);
   L.list = off;
   off = round_up(off + qrows * (size_t)(topk > 0 ? topk : 1) * sizeof(int32_t), 256);
   L.count = off;
@@ -647,6 +653,9 @@ int attn_dsa_decode(const attn_shape_t* shape, const void* q, attn_strides_t q_s
   A.Hi = index_heads;
   A.topk = topk;
   A.scores = reinterpret_cast<float*>(ws + L.scores);
+  A.ebound = reinterpret_cast<float*>(ws + L.ebound);
+  A.s64 = reinterpret_cast<double*>(ws + L.s64);
+  A.band = reinterpret_cast<int32_t*>(ws + L.band);
   A.list = kept_list ? kept_list : reinterpret_cast<int32_t*>(ws + L.list);
   A.count = kept_count ? kept_count : reinterpret_cast<int32_t*>(ws + L.count);
   A.idx_waves = 12 * device_cus();  // three single-wave workgroups per SIMD (148 VGPRs each)

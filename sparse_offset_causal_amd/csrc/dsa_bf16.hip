@@ -44,6 +44,7 @@ constexpr float RESCALE_SLACK = 8.0f;
 
 typedef short s16x4 __attribute__((__vector_size__(8)));
 typedef short s16x8 __attribute__((__vector_size__(16)));
+typedef double f64x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
 
@@ -64,6 +65,14 @@ __device__ __forceinline__ float row16_sum(float x) {
   x += dpp_f32<0x140>(x);  // row_mirror
   return x;
 }
+// The smallest bf16 value >= x (x >= 0, finite).
+__device__ __forceinline__ bf16_t bf16_round_up(float x) {
+  uint32_t u = __builtin_bit_cast(uint32_t, x);
+  if (u & 0xffffu) u += 0x10000u;
+  return __builtin_bit_cast(bf16_t, (uint16_t)(u >> 16));
+}
+// Covers the fp32 rounding of the sum that forms u before it is rounded up (64 terms).
+constexpr float kBoundSumSlack = 1.0f + 0x1p-16f;
 __device__ __forceinline__ uint32_t f32_order_key(float x) {
   const uint32_t u = __builtin_bit_cast(uint32_t, x);
   return (u >> 31) ? ~u : (u | 0x80000000u);
@@ -89,6 +98,7 @@ __device__ __forceinline__ int wave_incl_prefix_i(int x) {
 
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) dsa_indexer_kernel(DsaArgs A) {
   const AttnArgs& a = A.at;
+  __shared__ __attribute__((aligned(16))) bf16_t ulds[DI];
   const int lane = threadIdx.x, G = lane >> 4, i16 = lane & 15;
   const int rows = a.B * a.tq;
   // Row r = b * tq + t has nb(r) = ceil(n_vis / 16) blocks of 16 tokens; the blocks of all
@@ -139,10 +149,27 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) ds
       for (int ks = 0; ks < 4; ++ks) qb[hb][ks] = ok ? *(const bf16x8*)(qp + 32 * ks + 8 * G) : as_bf16x8(z);
       w[hb] = ok ? A.wi[((int64_t)b * A.Hi + head) * a.tq + t] : 0.f;
     }
+    // Error-bound weights u[d] = sum_j |w_j| |qi_j[d]| of this query token, rounded up to bf16,
+    // kept in LDS (ulds) and read as a B operand broadcast to all 16 columns: the MFMA of |k|
+    // against it gives E = u . |k|, which bounds the fp32 rounding of the token's score.
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8 uv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float p = 0.f;
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) p = fmaf(fabsf(w[hb]), fabsf((float)qb[hb][ks][e]), p);
+        uv[e] = bf16_round_up(row16_sum(p) * kBoundSumSlack);
+      }
+      if (i16 == 0) *(bf16x8*)(ulds + 32 * ks + 8 * G) = uv;
+    }
     const bf16_t* kp = (const bf16_t*)A.ki + b * A.ki_sb;
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kp, (short)0, (int)(n_vis * row_bytes), 0x00020000);
     float* out = A.scores + ((int64_t)b * a.tq + t) * a.tk;
     const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc((void*)out, (short)0, (int)(n_vis * 4), 0x00020000);
+    float* eout = A.ebound + ((int64_t)b * a.tq + t) * a.tk;
+    const __amdgpu_buffer_rsrc_t ers = __builtin_amdgcn_make_buffer_rsrc((void*)eout, (short)0, (int)(n_vis * 4), 0x00020000);
     const int j0 = g - rstart, j1 = min(nb_row, hi - rstart);  // this wave's blocks of the row
     auto load = [&](bf16x8* af, int j) __attribute__((always_inline)) {
       const int tok0 = 16 * j;
@@ -169,10 +196,19 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) ds
       // (no branch, so the compiler can keep counting the key loads still in flight).
 #pragma unroll
       for (int v = 0; v < 4; ++v) part[v] = row16_sum(part[v]);
+      // E = u . |k| for tokens 4G + v (every column; lanes i16 == 0 store it).  The empty asm
+      // makes the LDS address opaque, so the reads stay here instead of holding u in registers.
+      const bf16_t* ua = ulds + 8 * G;
+      asm volatile("" : "+v"(ua));
+      f32x4 eacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        eacc = mfma16k32(as_bf16x8(as_u32x4(af[ks]) & 0x7fff7fffu), *(const bf16x8*)(ua + 32 * ks), eacc);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const uint32_t at = i16 == 0 ? (uint32_t)(tok0 + 4 * G + v) * 4u : 0x80000000u;
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, part[v]), ors, at, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, eacc[v]), ers, at, 0, 0);
       }
     };
     // the keys of blocks j + 1 and j + 2 are in flight while block j is scored (three
@@ -248,13 +284,53 @@ __device__ void locate_digit(const unsigned* hist, unsigned rank, unsigned* digi
 }
 
 constexpr int TOPK_LDS = 32768;  // scores of up to this many visible tokens are staged in LDS
-constexpr int TOPK_BINS = 4096;  // digits of 12, 12 and 8 bits
+constexpr int TOPK_BINS = 4096;  // digits of 12, 12 and 8 bits (32-bit keys); 12 x 4, 8 x 2 (64-bit)
+
+// |fp32 score - exact score| <= kScoreErrBound * E for every token (E = u . |k| from the
+// indexer).  Each head's 128-term dot product is accumulated in fp32 (relative error at most
+// 128 * 2^-24 of sum |q_d k_d|), and the weighted ReLU terms are summed over at most 64 heads
+// with at most 8 roundings (2^-21 of sum |w_j relu(dot_j)|, itself <= E); together below
+// 2^-16 * E.  The bound used is 4x that, which also covers E's own fp32 rounding and an MFMA
+// that accumulated with twice the rounding error of round-to-nearest.
+constexpr double kScoreErrBound = 0x1p-14;
+
+__device__ __forceinline__ uint64_t f64_key(double x) { return f64_order_key(x); }
+
+// Block-wide sums and maxima over the 16 waves of the top-k workgroup (through `red`, 16 slots).
+__device__ __forceinline__ unsigned block_sum_u(unsigned x, unsigned* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  __syncthreads();
+  if (lane == 0) red[wave] = x;
+  __syncthreads();
+  unsigned t = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) t += red[w];
+  return t;
+}
+__device__ __forceinline__ float block_max_f(float x, unsigned* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  __syncthreads();
+  if (lane == 0) red[wave] = __builtin_bit_cast(unsigned, x);
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) t = fmaxf(t, __builtin_bit_cast(float, red[w]));
+  return t;
+}
+
+constexpr int BAND_LDS = 1024;  // band sizes decided in LDS; larger bands by fp64 radix select
 
 __global__ void __launch_bounds__(1024) dsa_topk_kernel(DsaArgs A) {
   const AttnArgs& a = A.at;
-  __shared__ unsigned hist[TOPK_BINS];
+  __shared__ __attribute__((aligned(8))) unsigned hist[TOPK_BINS];
   __shared__ unsigned su[2];
   __shared__ unsigned wcnt[2][16];
+  __shared__ unsigned red[16];
+  __shared__ unsigned nband_s;
   __shared__ uint32_t keys[TOPK_LDS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t = blockIdx.x % a.tq, b = blockIdx.x / a.tq;
@@ -266,25 +342,37 @@ __global__ void __launch_bounds__(1024) dsa_topk_kernel(DsaArgs A) {
     if (tid == 0) A.count[b * a.tq + t] = n_vis;
     return;
   }
-  const float* sc = A.scores + ((int64_t)b * a.tq + t) * a.tk;
+  const int64_t row_off = ((int64_t)b * a.tq + t) * a.tk;
+  const float* sc = A.scores + row_off;
+  const float* eb = A.ebound + row_off;
+  double* s64 = A.s64 + row_off;
+  int32_t* band = A.band + row_off;
   const bool staged = n_vis <= TOPK_LDS;
   auto key_at = [&](int i) __attribute__((always_inline)) { return staged ? keys[i] : f32_order_key(sc[i]); };
+  auto f32_of_key = [](uint32_t k) __attribute__((always_inline)) {
+    return __builtin_bit_cast(float, (k >> 31) ? (k & 0x7fffffffu) : ~k);
+  };
 
-  // Radix select of the key at descending rank K - 1: the histogram of the top 12 bits is
-  // built while the keys are staged, then bits 19..8 and 7..0 among the keys that share the
-  // digits chosen so far.
+  // 1. The fp32 threshold tau32 (the key at descending rank K - 1) by radix select: the
+  // histogram of the top 12 bits is built while the keys are staged (and the largest error
+  // bound taken), then bits 19..8 and 7..0 among the keys that share the digits chosen so far.
   for (int i = tid; i < TOPK_BINS; i += 1024) hist[i] = 0;
+  if (tid == 0) nband_s = 0;
   __syncthreads();
+  float emax = 0.f;
   for (int i0 = tid; i0 < n_vis; i0 += 4 * 1024) {
     uint32_t kv[4];
+    float ev[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int i = i0 + 1024 * u;
       kv[u] = i < n_vis ? f32_order_key(sc[i]) : 0u;
+      ev[u] = i < n_vis ? eb[i] : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int i = i0 + 1024 * u;
+      emax = fmaxf(emax, ev[u]);
       if (i < n_vis) {
         if (staged) keys[i] = kv[u];
         atomicAdd(&hist[kv[u] >> 20], 1u);
@@ -292,8 +380,8 @@ __global__ void __launch_bounds__(1024) dsa_topk_kernel(DsaArgs A) {
     }
   }
   __syncthreads();
-  unsigned prefix = 0, pmask = 0, rank = (unsigned)(K - 1);
-  auto choose = [&](auto nb_tag, int shift, unsigned dmask) __attribute__((always_inline)) {
+  unsigned rank = (unsigned)(K - 1);
+  auto pick = [&](auto nb_tag) __attribute__((always_inline)) -> unsigned {  // digit; updates rank
     constexpr int NB = decltype(nb_tag)::value;
     if (wave == 0) {
       unsigned dg, r;
@@ -304,11 +392,12 @@ __global__ void __launch_bounds__(1024) dsa_topk_kernel(DsaArgs A) {
       }
     }
     __syncthreads();
-    prefix |= su[0] << shift;
-    pmask |= dmask << shift;
+    const unsigned dg = su[0];
     rank = su[1];
+    return dg;
   };
-  auto count_digit = [&](int shift, unsigned dmask, int nb) __attribute__((always_inline)) {
+  uint32_t prefix = 0, pmask = 0;
+  auto count32 = [&](int shift, unsigned dmask, int nb) __attribute__((always_inline)) {
     for (int i = tid; i < nb; i += 1024) hist[i] = 0;
     __syncthreads();
     for (int i = tid; i < n_vis; i += 1024) {
@@ -317,26 +406,183 @@ __global__ void __launch_bounds__(1024) dsa_topk_kernel(DsaArgs A) {
     }
     __syncthreads();
   };
-  choose(std::integral_constant<int, 4096>{}, 20, 0xfffu);
-  count_digit(8, 0xfffu, 4096);
-  choose(std::integral_constant<int, 4096>{}, 8, 0xfffu);
-  count_digit(0, 0xffu, 256);
-  choose(std::integral_constant<int, 256>{}, 0, 0xffu);
+  prefix |= pick(std::integral_constant<int, 4096>{}) << 20;
+  pmask |= 0xfffu << 20;
+  count32(8, 0xfffu, 4096);
+  prefix |= pick(std::integral_constant<int, 4096>{}) << 8;
+  pmask |= 0xfffu << 8;
+  count32(0, 0xffu, 256);
+  prefix |= pick(std::integral_constant<int, 256>{});
+  const double tau32 = (double)f32_of_key(prefix);
 
-  // Ordered compaction: keys above the threshold, then the first rank + 1 keys equal to it in
-  // token order.  Wave w owns a contiguous segment of tokens; one count pass and one barrier
-  // give every wave its output offset, a second pass writes the indices in order.
-  const uint32_t tau = prefix;
-  const unsigned need_eq = rank + 1;
+  // 2. The exact decision.  Every token's fp32 score is within D = max_i kScoreErrBound * E_i
+  // of its exact score, so the exact K-th largest score lies within D of tau32: a token with
+  // s32 > tau32 + 2D is kept for certain, one with s32 < tau32 - 2D dropped for certain, and
+  // the tokens in between (the band, never empty) are scored again in fp64 and decided by
+  // that score.  The kept set is then the top K of the fp64 scores, equal scores to the lower
+  // token index.
+  const double bw = 2.0 * kScoreErrBound * (double)block_max_f(emax, red);
+  auto certain = [&](uint32_t key) __attribute__((always_inline)) -> int {  // 2 kept, 0 dropped, 1 band
+    const double s32 = (double)f32_of_key(key);
+    return s32 > tau32 + bw ? 2 : s32 < tau32 - bw ? 0 : 1;
+  };
+  // the band in small rows lives in LDS, in the histogram's space (free from here on)
+  uint64_t* bkey = reinterpret_cast<uint64_t*>(hist);
+  int32_t* bidx = reinterpret_cast<int32_t*>(hist + 2 * BAND_LDS);
+  static_assert(3 * BAND_LDS <= TOPK_BINS, "band arrays fit in the histogram's LDS");
+  unsigned n_in = 0;
+  for (int i0 = 0; i0 < n_vis; i0 += 1024) {
+    const int i = i0 + tid;
+    const int c = i < n_vis ? certain(key_at(i)) : 0;
+    n_in += c == 2;
+    const unsigned long long bb = __ballot(c == 1);
+    unsigned base = 0;
+    if (lane == 0 && bb) base = atomicAdd(&nband_s, (unsigned)__popcll(bb));
+    base = __builtin_amdgcn_readfirstlane(base);
+    if (c == 1) {
+      const unsigned e = base + (unsigned)__popcll(bb & ((1ull << lane) - 1ull));
+      band[e] = i;
+      if (e < BAND_LDS) bidx[e] = i;
+    }
+  }
+  n_in = block_sum_u(n_in, red);  // (its barriers also publish nband_s and the band lists)
+  const int n_band = (int)nband_s;
+  const bool in_lds = n_band <= BAND_LDS;
+  const int R = K - (int)n_in;  // band tokens to keep (>= 1)
+
+  // fp64 scores of the band on the fp64 MFMA (v_mfma_f64_16x16x4f64: A[i][k] in lane i + 16k,
+  // B[k][j] in lane j + 16k, D[i][j] in lane j + 16 (i % 4), element i / 4).  A wave takes 16
+  // band tokens (rows i) and the indexer heads 16 at a time (columns j); lane (slot, G) feeds
+  // dims 32G + m of its token's key and of its head's query at step m = 0..31, so the 32 steps
+  // sum all 128 dims.  ReLU and the head weight apply to each full dot product, the heads of a
+  // tile are summed across their 16 lanes and the tiles in order: a fixed order throughout, so
+  // equal key rows get equal scores.
+  {
+    const int Hi = A.Hi;
+    const int slot = lane & 15, G = lane >> 4;
+    const bf16_t* kbase = (const bf16_t*)A.ki + b * A.ki_sb;
+    const int ngroups = (n_band + 15) / 16;
+    for (int grp = wave; grp < ngroups; grp += 16) {
+      const int e = min(grp * 16 + slot, n_band - 1);  // slots past the band repeat its last token
+      const int tok = in_lds ? bidx[e] : band[e];
+      const u32x4* kp = (const u32x4*)(kbase + (int64_t)tok * A.ki_st + 32 * G);
+      double sacc[4] = {0.0, 0.0, 0.0, 0.0};  // tokens 4v + G
+      for (int ht = 0; ht < Hi; ht += 16) {
+        const int head = ht + slot;
+        const bool hok = head < Hi;
+        const u32x4* qp = (const u32x4*)((const bf16_t*)A.qi + b * A.qi_sb + (hok ? head : 0) * A.qi_sh + t * A.qi_st + 32 * G);
+        const double wj = hok ? (double)A.wi[((int64_t)b * Hi + head) * a.tq + t] : 0.0;
+        f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll 1
+        for (int c = 0; c < 4; ++c) {  // 8 steps per 16 bytes of key and query (L1 hits after the first tile)
+          const u32x4 kc = kp[c];
+          const u32x4 qc = hok ? qp[c] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+          for (int m = 0; m < 8; ++m) {
+            const uint32_t kw = kc[m >> 1], qw2 = qc[m >> 1];
+            const double av = (double)((m & 1) ? bf16_hi(kw) : bf16_lo(kw));
+            const double bv = (double)((m & 1) ? bf16_hi(qw2) : bf16_lo(qw2));
+            acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc, 0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          double term = wj * (acc[v] > 0.0 ? acc[v] : 0.0);
+#pragma unroll
+          for (int o = 1; o < 16; o <<= 1) term += __shfl_xor(term, o, 64);  // the tile's 16 heads
+          sacc[v] += term;
+        }
+      }
+      if (slot == 0) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int ei = grp * 16 + 4 * v + G;
+          if (ei < n_band) {
+            if (in_lds)
+              bkey[ei] = f64_key(sacc[v]);
+            else
+              s64[band[ei]] = sacc[v];
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  uint64_t tau64 = 0;
+  unsigned need_eq = 0;
+  if (in_lds) {
+    // Each band token's rank in (fp64 score descending, token index ascending); the first R
+    // are kept.  The decision is written over the token's fp32 key (+inf kept, -inf dropped),
+    // so the compaction below classifies every token from its key alone.
+    constexpr uint32_t KEY_POS_INF = 0xff800000u, KEY_NEG_INF = 0x007fffffu;  // f32_order_key(+-inf)
+    uint32_t dec = 0;
+    int itok = -1;
+    if (tid < n_band) {
+      const uint64_t ke = bkey[tid];
+      itok = bidx[tid];
+      int rk = 0;
+      for (int f = 0; f < n_band; ++f) {
+        const uint64_t kf = bkey[f];
+        rk += (kf > ke) | ((kf == ke) & (bidx[f] < itok));
+      }
+      dec = rk < R ? KEY_POS_INF : KEY_NEG_INF;
+    }
+    __syncthreads();  // every rank is taken before any key changes
+    if (itok >= 0) {
+      if (staged)
+        keys[itok] = dec;
+      else
+        const_cast<float*>(sc)[itok] = f32_of_key(dec);
+    }
+  } else {
+    // fp64 radix select over the band: descending rank R - 1 (digits of 12 x 4, 8 x 2)
+    rank = (unsigned)max(0, min(R - 1, n_band - 1));
+    uint64_t p64 = 0, m64 = 0;
+    auto count64 = [&](int shift, unsigned dmask, int nb) __attribute__((always_inline)) {
+      for (int i = tid; i < nb; i += 1024) hist[i] = 0;
+      __syncthreads();
+      for (int e = tid; e < n_band; e += 1024) {
+        const uint64_t key = f64_key(s64[band[e]]);
+        if ((key & m64) == p64) atomicAdd(&hist[(unsigned)(key >> shift) & dmask], 1u);
+      }
+      __syncthreads();
+    };
+#pragma unroll 1
+    for (int shift = 52; shift >= 16; shift -= 12) {
+      count64(shift, 0xfffu, 4096);
+      p64 |= (uint64_t)pick(std::integral_constant<int, 4096>{}) << shift;
+      m64 |= (uint64_t)0xfff << shift;
+    }
+#pragma unroll 1
+    for (int shift = 8; shift >= 0; shift -= 8) {
+      count64(shift, 0xffu, 256);
+      p64 |= (uint64_t)pick(std::integral_constant<int, 256>{}) << shift;
+      m64 |= (uint64_t)0xff << shift;
+    }
+    tau64 = p64;
+    need_eq = rank + 1;
+  }
+  __syncthreads();
+
+  // 3. Ordered compaction: every token kept for certain or by its fp64 score, then (large
+  // bands) the first need_eq band tokens equal to tau64 in token order.  Wave w owns a
+  // contiguous segment of tokens; one count pass and one barrier give every wave its output
+  // offset, a second pass writes the indices in order.
+  auto cls_at = [&](int i) __attribute__((always_inline)) -> int {  // 2 keep, 1 tie at tau64, 0 drop
+    const int c = certain(key_at(i));
+    if (c != 1 || in_lds) return c;  // (small bands: already decided in the keys)
+    const uint64_t k64 = f64_key(s64[i]);
+    return k64 > tau64 ? 2 : k64 == tau64 ? 1 : 0;
+  };
   const int seg = ((n_vis + 16 * 64 - 1) / (16 * 64)) * 64;
   const int w0 = wave * seg, w1 = min(w0 + seg, n_vis);
   unsigned gt_c = 0, eq_c = 0;
   for (int c0 = w0; c0 < w0 + seg; c0 += 64) {
     const int i = c0 + lane;
-    const bool in = i < w1;
-    const uint32_t key = in ? key_at(i) : 0u;
-    gt_c += (unsigned)__popcll(__ballot(in && key > tau));
-    eq_c += (unsigned)__popcll(__ballot(in && key == tau));
+    const int c = i < w1 ? cls_at(i) : 0;
+    gt_c += (unsigned)__popcll(__ballot(c == 2));
+    eq_c += (unsigned)__popcll(__ballot(c == 1));
   }
   if (lane == 0) {
     wcnt[0][wave] = gt_c;
@@ -353,11 +599,9 @@ __global__ void __launch_bounds__(1024) dsa_topk_kernel(DsaArgs A) {
   const unsigned long long lt_mask = (1ull << lane) - 1ull;
   for (int c0 = w0; c0 < w0 + seg; c0 += 64) {
     const int i = c0 + lane;
-    const bool in = i < w1;
-    const uint32_t key = in ? key_at(i) : 0u;
-    const bool gt = in && key > tau, eq = in && key == tau;
-    const unsigned long long beq = __ballot(eq);
-    const bool keep = gt || (eq && eq_seen + (unsigned)__popcll(beq & lt_mask) < need_eq);
+    const int c = i < w1 ? cls_at(i) : 0;
+    const unsigned long long beq = __ballot(c == 1);
+    const bool keep = c == 2 || (c == 1 && eq_seen + (unsigned)__popcll(beq & lt_mask) < need_eq);
     const unsigned long long bk = __ballot(keep);
     const unsigned pos = out + (unsigned)__popcll(bk & lt_mask);
     if (keep && pos < (unsigned)K) lst[pos] = i;

@@ -140,7 +140,10 @@ struct DsaArgs {
   int64_t ki_sb, ki_st;
   const float* wi;      // [B, Hi, tq]
   int32_t Hi, topk;
-  float* scores;        // workspace [B, tq, tk]
+  float* scores;        // workspace [B, tq, tk]  fp32 indexer scores
+  float* ebound;        // workspace [B, tq, tk]  E = u . |k| per token (bounds the fp32 score error)
+  double* s64;          // workspace [B, tq, tk]  fp64 scores of the tokens near the threshold
+  int32_t* band;        // workspace [B, tq, tk]  those tokens' indices (any order)
   int32_t* list;        // [B, tq, topk] kept token indices, ascending
   int32_t* count;       // [B, tq]
   int32_t idx_waves;    // waves of the indexer grid (each scores an equal share of all blocks)
