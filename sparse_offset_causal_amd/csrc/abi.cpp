@@ -136,7 +136,7 @@ size_t round_up(size_t x, size_t m) { return (x + m - 1) / m * m; }
 
 struct SelectLayout {
   int nqb, nkb;
-  size_t qmean, cT, rad2, score, norm2, nmax, hpart, tflag, hist, ccount, pick, cand, total;  // byte offsets, total
+  size_t qmean, cT, rad2, score, norm2, nmax, hpart, tflag, ccount, pick, cand, total;  // byte offsets, total
 };
 
 SelectLayout select_layout(const attn_shape_t* s, int bs) {
@@ -164,10 +164,8 @@ SelectLayout select_layout(const attn_shape_t* s, int bs) {
   off = round_up(off + sizeof(uint16_t) * bh * tiles * soc::kSelBuckets, 256);
   L.tflag = off;
   off = round_up(off + sizeof(uint32_t) * bh * tiles, 256);
-  L.hist = off;
-  off = round_up(off + sizeof(uint32_t) * bh * soc::kSelBuckets, 256);
   L.ccount = off;
-  off = round_up(off + sizeof(uint32_t) * bh, 256);
+  off = round_up(off + sizeof(uint32_t) * bh * (((size_t)L.nqb * L.nkb + soc::kSelGatherChunk - 1) / soc::kSelGatherChunk), 256);
   L.pick = off;
   off = round_up(off + sizeof(int64_t) * bh * 4, 256);
   L.cand = off;
@@ -729,14 +727,13 @@ int attn_block_select(const attn_shape_t* shape, const void* q, attn_strides_t q
   a.list = block_list;
   char* ws = static_cast<char*>(workspace);
   a.qmean = reinterpret_cast<double*>(ws + L.qmean);
-  a.cT = reinterpret_cast<double*>(ws + L.cT);
+  a.cent = reinterpret_cast<double*>(ws + L.cT);
   a.rad2 = reinterpret_cast<double*>(ws + L.rad2);
   a.score = reinterpret_cast<double*>(ws + L.score);
   a.norm2 = reinterpret_cast<double*>(ws + L.norm2);
   a.nmax = reinterpret_cast<double*>(ws + L.nmax);
   a.hpart = reinterpret_cast<uint32_t*>(ws + L.hpart);
   a.tflag = reinterpret_cast<uint32_t*>(ws + L.tflag);
-  a.hist = reinterpret_cast<uint32_t*>(ws + L.hist);
   a.ccount = reinterpret_cast<uint32_t*>(ws + L.ccount);
   a.pick = reinterpret_cast<int64_t*>(ws + L.pick);
   a.cand = reinterpret_cast<double*>(ws + L.cand);

@@ -3,27 +3,27 @@
 // Steps, in the order of the patty.io review of RBS-Attention (sections on the centroid
 // score, mean dilution, the max-key-radius signal, the two independently thresholded
 // branches and their union):
-//   1. qmean_kernel   mean of the query rows of every (b, h, query block)
-//   2. kstats_kernel  centroid of every (b, kv, key block) and its squared radius, the
-//                     largest |k_j - c|^2 over the block's keys
-//   3. score_kernel   s1 = <qmean, c> for admissible (query block, key block) pairs,
-//                     -inf elsewhere (admissible = holds at least one (row, key) pair the
-//                     position / window rule allows); 64 x 64 tiles of s1 per workgroup
+//   1-2. stats_kernel  in one grid: the mean of the query rows of every (b, h, query block),
+//                      and the centroid of every (b, kv, key block) with its squared radius,
+//                      the largest |k_j - c|^2 over the block's keys
+//   3. score_kernel    s1 = <qmean, c> for admissible (query block, key block) pairs, -inf
+//                      elsewhere (admissible = holds at least one (row, key) pair the position /
+//                      window rule allows); 64 x 64 tiles on the fp64 MFMA
 //   4. the per-head order statistic of s1 and the per-(b, kv) one of rad2 at the keep
 //      fractions: with N values and n = floor(keep*N + 1/2), tau = the (n+1)-th largest
 //      (-inf if n >= N), found exactly:
 //        score_kernel   also counts the admissible s1 of its tile into a value histogram
 //                       (a monotone bucket map over [-M, M], M = max|qmean| * max|c|, the
 //                       Cauchy-Schwarz bound; values outside clamp to the end buckets)
-//        hist_reduce_kernel  sums the tile histograms of each head
-//        gather_kernel  locates the bucket holding descending rank n and copies that
-//                       bucket's values out (a few dozen on typical data)
+//        pick_kernel    sums the tile histograms of each head and locates the bucket holding
+//                       descending rank n and the rank inside it
+//        gather_kernel  copies that bucket's values out (a few dozen on typical data)
 //        threshold_kernel  radix select on order-preserving 64-bit keys among the copied
 //                       values (and among the rad2 of each (b, kv))
 //      A monotone map puts every value of a higher bucket strictly above every value of a
 //      lower one, so rank n overall is rank n - (count above the bucket) inside it.
 //   5. mask_kernel    mask = admissible and (s1 > tau_mean or rad2 > tau_radius), plus the
-//                     ascending list of kept key blocks per (b, h, query block)
+//                     ascending list of kept key blocks per (b, h, query block), one wave per row
 // bf16 and f32 inputs widen exactly to f64.  Every reduction that feeds a value has a fixed
 // order, so the output is identical from run to run; means are sums of at most a few hundred
 // short mantissas and come out exact, so they agree bit for bit with any correct f64
@@ -138,12 +138,10 @@ __device__ __forceinline__ void write_norm2(const double* v, double* dst) {
 }
 
 template <typename T, int D>
-__global__ void __launch_bounds__(NTHR) qmean_kernel(SelectArgs a) {
-  __shared__ double red[NTHR * 8];
-  __shared__ double mean[D];
-  const int qb = blockIdx.x % a.nqb;
-  const int h = (blockIdx.x / a.nqb) % a.Hq;
-  const int b = blockIdx.x / (a.nqb * a.Hq);
+__device__ __forceinline__ void qmean_block(const SelectArgs& a, int id, double* red, double* mean) {
+  const int qb = id % a.nqb;
+  const int h = (id / a.nqb) % a.Hq;
+  const int b = id / (a.nqb * a.Hq);
   const int64_t bh = (int64_t)b * a.Hq + h;
   const T* base = (const T*)a.q + b * a.q_sb + h * a.q_sh;
   Row8<T> rows[RB];
@@ -153,17 +151,14 @@ __global__ void __launch_bounds__(NTHR) qmean_kernel(SelectArgs a) {
 }
 
 template <typename T, int D>
-__global__ void __launch_bounds__(NTHR) kstats_kernel(SelectArgs a) {
-  __shared__ double red[NTHR * 8];
-  __shared__ double cent[D];
-  __shared__ double rmax[NTHR / 64];
-  const int kb = blockIdx.x % a.nkb;
-  const int kvh = (blockIdx.x / a.nkb) % a.Hkv;
-  const int b = blockIdx.x / (a.nkb * a.Hkv);
+__device__ __forceinline__ void kstats_block(const SelectArgs& a, int id, double* red, double* cent, double* rmax) {
+  const int kb = id % a.nkb;
+  const int kvh = (id / a.nkb) % a.Hkv;
+  const int b = id / (a.nkb * a.Hkv);
   const int tkb = seq_off(a, b) + a.tq;
-  double* cT = a.cT + ((int64_t)b * a.Hkv + kvh) * D * a.nkb;
+  double* crow = a.cent + (((int64_t)b * a.Hkv + kvh) * a.nkb + kb) * D;  // centroids row-major
   if (kb * a.bs >= tkb) {  // block beyond this sequence's keys
-    if (threadIdx.x < D) cT[(int64_t)threadIdx.x * a.nkb + kb] = 0.0;
+    if (threadIdx.x < D) crow[threadIdx.x] = 0.0;
     if (threadIdx.x == 0) {
       a.rad2[((int64_t)b * a.Hkv + kvh) * a.nkb + kb] = SOC_NEG_INF;
       if (a.keep_mean >= 0.0) a.norm2[(int64_t)a.B * a.Hq * a.nqb + ((int64_t)b * a.Hkv + kvh) * a.nkb + kb] = 0.0;
@@ -174,7 +169,7 @@ __global__ void __launch_bounds__(NTHR) kstats_kernel(SelectArgs a) {
   const int r0 = kb * a.bs, r1 = min((kb + 1) * a.bs, tkb);
   Row8<T> rows[RB];
   const bool kept = block_mean<T, D>(base, a.k_st, r0, r1, red, cent, rows);
-  if (threadIdx.x < D) cT[(int64_t)threadIdx.x * a.nkb + kb] = cent[threadIdx.x];
+  if (threadIdx.x < D) crow[threadIdx.x] = cent[threadIdx.x];
   if (a.keep_mean >= 0.0)
     write_norm2<D>(cent, a.norm2 + (int64_t)a.B * a.Hq * a.nqb + ((int64_t)b * a.Hkv + kvh) * a.nkb + kb);
 
@@ -219,8 +214,21 @@ __global__ void __launch_bounds__(NTHR) kstats_kernel(SelectArgs a) {
     a.rad2[((int64_t)b * a.Hkv + kvh) * a.nkb + kb] = fmax(fmax(rmax[0], rmax[1]), fmax(rmax[2], rmax[3]));
 }
 
-// Per head (first B*Hq blocks) the largest |qmean|^2, per (b, kv) the largest |c|^2; the
-// head blocks also clear the head's candidate counter.
+// Steps 1 and 2 in one grid: the first B*Hq*nqb workgroups take query blocks, the rest key
+// blocks, so the key blocks' second (radius) pass hides inside the query stream.
+template <typename T, int D>
+__global__ void __launch_bounds__(NTHR) stats_kernel(SelectArgs a) {
+  __shared__ double red[NTHR * 8];
+  __shared__ double vec[D];
+  __shared__ double rmax[NTHR / 64];
+  const int nq = a.B * a.Hq * a.nqb;
+  if ((int)blockIdx.x < nq)
+    qmean_block<T, D>(a, blockIdx.x, red, vec);
+  else
+    kstats_block<T, D>(a, blockIdx.x - nq, red, vec, rmax);
+}
+
+// Per head (first B*Hq blocks) the largest |qmean|^2, per (b, kv) the largest |c|^2.
 __global__ void __launch_bounds__(NTHR) norm_max_kernel(SelectArgs a) {
   __shared__ double wm[NTHR / 64];
   const int64_t nbh = (int64_t)a.B * a.Hq;
@@ -236,7 +244,6 @@ __global__ void __launch_bounds__(NTHR) norm_max_kernel(SelectArgs a) {
   __syncthreads();
   if (threadIdx.x == 0) {
     a.nmax[id] = fmax(fmax(wm[0], wm[1]), fmax(wm[2], wm[3]));
-    if (qside) a.ccount[id] = 0;
   }
 }
 
@@ -260,13 +267,19 @@ struct BucketMap {
 };
 
 constexpr int ST = kScoreTile;
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+typedef double f64x2 __attribute__((ext_vector_type(2)));
 
+// s1 = <qmean, c> on the fp64 MFMA (v_mfma_f64_16x16x4f64: A[i][k] in lane i + 16k, B[k][j]
+// in lane j + 16k, D[i][j] in lane j + 16 (i % 4), element i / 4), one 64 x 64 tile of
+// (query block, key block) pairs per workgroup, a 32 x 32 quarter (2 x 2 MFMA tiles) per
+// wave; the D/4 steps sum all D dims, each lane reading contiguous 16-byte pieces of its row.  The same pass counts every
+// admissible s1 of the tile into a value histogram under the monotone bucket map.
 template <int D>
 __global__ void __launch_bounds__(NTHR) score_kernel(SelectArgs a) {
-  constexpr int SD = D < 32 ? D : 32;  // head-dim slice staged per step
-  __shared__ double qs[ST][SD + 1];    // +1: the four rows a wave reads land in distinct banks
-  __shared__ double cs[SD][ST];
   __shared__ uint32_t hist[kSelBuckets];
+  __shared__ __attribute__((aligned(16))) double qstage[64 * ((D < 32 ? D : 32) + 2)];
+  __shared__ __attribute__((aligned(16))) double cstage[64 * ((D < 32 ? D : 32) + 2)];
   const int ntq = (a.nqb + ST - 1) / ST, ntk = (a.nkb + ST - 1) / ST;
   int id = blockIdx.x;
   const int tkt = id % ntk;
@@ -277,93 +290,114 @@ __global__ void __launch_bounds__(NTHR) score_kernel(SelectArgs a) {
   const int kvh = h / a.g;
   const int64_t bh = (int64_t)b * a.Hq + h, bkv = (int64_t)b * a.Hkv + kvh;
   const int off = seq_off(a, b), tkb = off + a.tq;
-  const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
-  const int QB0 = tqt * ST, KB0 = tkt * ST;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int li = lane & 15, lk = lane >> 4;
+  const int WR = tqt * ST + 32 * (wave >> 1), WC = tkt * ST + 32 * (wave & 1);
   const bool hist_on = a.keep_mean >= 0.0;
   double* out = a.score + bh * a.nqb * a.nkb;
 
-  // this thread's outputs: (QB0 + ty + 16 i, KB0 + tx + 16 j)
+  // this lane's outputs (r, c, v): qb = WR + 16 r + 4 v + lk, kb = WC + 16 c + li; bit (2r + c) * 4 + v
   unsigned adm = 0, inr = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int r = 0; r < 2; ++r)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int qb = QB0 + ty + 16 * i, kb = KB0 + tx + 16 * j;
-      const bool in = qb < a.nqb && kb < a.nkb;
-      inr |= (unsigned)in << (4 * i + j);
-      adm |= (unsigned)(in && admissible(a, off, tkb, qb, kb)) << (4 * i + j);
-    }
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int qb = WR + 16 * r + 4 * v + lk, kb = WC + 16 * c + li;
+        const bool in = qb < a.nqb && kb < a.nkb;
+        const int bit = (2 * r + c) * 4 + v;
+        inr |= (unsigned)in << bit;
+        adm |= (unsigned)(in && admissible(a, off, tkb, qb, kb)) << bit;
+      }
   const int64_t tile = (int64_t)bh * ntq * ntk + (int64_t)tqt * ntk + tkt;
   const bool active = __syncthreads_or(adm != 0);
   if (hist_on && threadIdx.x == 0) a.tflag[tile] = active;
+  auto out_at = [&](int r, int c, int v) __attribute__((always_inline)) -> double& {
+    return out[(int64_t)(WR + 16 * r + 4 * v + lk) * a.nkb + WC + 16 * c + li];
+  };
   if (!active) {  // nothing admissible in the tile
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int r = 0; r < 2; ++r)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (inr >> (4 * i + j) & 1) out[(int64_t)(QB0 + ty + 16 * i) * a.nkb + KB0 + tx + 16 * j] = SOC_NEG_INF;
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (inr >> ((2 * r + c) * 4 + v) & 1) out_at(r, c, v) = SOC_NEG_INF;
     return;
   }
   if (hist_on)
     for (int i = threadIdx.x; i < kSelBuckets; i += NTHR) hist[i] = 0;
 
-  const double* qm = a.qmean + bh * a.nqb * D;
-  const double* cT = a.cT + bkv * D * a.nkb;
-  double acc[4][4];
+  // Operands staged through LDS in 32-dim chunks (CD dims for small D): the workgroup's 64
+  // query-mean rows and 64 centroid rows (past the end: the last row; they feed only outputs
+  // that are never written), loaded whole-row-coalesced, the next chunk's loads in flight
+  // while the current one is used.  At step e of a chunk lane (i, k) feeds dim k*CD/4 + e.
+  constexpr int CD = D < 32 ? D : 32, E = CD / 4, RS = CD + 2;  // RS: padded row stride (doubles)
+  constexpr int NLD = 64 * CD / 2 / NTHR;  // 16-byte loads per thread per operand and chunk
+  const double* qsrc = a.qmean + bh * a.nqb * D;
+  const double* csrc = a.cent + bkv * a.nkb * D;
+  f64x2 qpre[NLD], cpre[NLD];
+  auto load_chunk = [&](int d0) __attribute__((always_inline)) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
-  // Staging: every thread loads NL values of each operand per head-dim slice into registers
-  // (rows and columns past the end are clamped to the last one; they feed only outputs that
-  // are never written), the next slice's loads in flight while the current one is computed.
-  constexpr int NL = ST * SD / NTHR;
-  double qr[NL], cr[NL];
-  auto load_slice = [&](int t0) __attribute__((always_inline)) {
-#pragma unroll
-    for (int k = 0; k < NL; ++k) {
-      const int i = threadIdx.x + k * NTHR;
-      const int qb = min(QB0 + i / SD, a.nqb - 1), kb = min(KB0 + i % ST, a.nkb - 1);
-      qr[k] = qm[(int64_t)qb * D + t0 + i % SD];
-      cr[k] = cT[(int64_t)(t0 + i / ST) * a.nkb + kb];
+    for (int u = 0; u < NLD; ++u) {
+      const int idx = threadIdx.x + u * NTHR;  // 16-byte piece of the 64 x CD chunk
+      const int row = idx / (CD / 2), pc = idx % (CD / 2);
+      qpre[u] = *(const f64x2*)(qsrc + (int64_t)min(tqt * ST + row, a.nqb - 1) * D + d0 + 2 * pc);
+      cpre[u] = *(const f64x2*)(csrc + (int64_t)min(tkt * ST + row, a.nkb - 1) * D + d0 + 2 * pc);
     }
   };
-  load_slice(0);
-  for (int t0 = 0; t0 < D; t0 += SD) {
+  f64x4 acc[2][2];
 #pragma unroll
-    for (int k = 0; k < NL; ++k) {
-      const int i = threadIdx.x + k * NTHR;
-      qs[i / SD][i % SD] = qr[k];
-      cs[i / ST][i % ST] = cr[k];
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) acc[r][c] = f64x4{0.0, 0.0, 0.0, 0.0};
+  load_chunk(0);
+  const int ar0 = 32 * (wave >> 1) + li, bc0 = 32 * (wave & 1) + li;  // this lane's rows in the stage
+#pragma unroll 1
+  for (int d0 = 0; d0 < D; d0 += CD) {
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const int idx = threadIdx.x + u * NTHR;
+      const int row = idx / (CD / 2), pc = idx % (CD / 2);
+      *(f64x2*)(qstage + row * RS + 2 * pc) = qpre[u];
+      *(f64x2*)(cstage + row * RS + 2 * pc) = cpre[u];
     }
     __syncthreads();
-    if (t0 + SD < D) load_slice(t0 + SD);
-#pragma unroll 8
-    for (int t = 0; t < SD; ++t) {  // s1 accumulates over the head dimension in ascending order
-      double qv[4], cv[4];
+    if (d0 + CD < D) load_chunk(d0 + CD);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) qv[i] = qs[ty + 16 * i][t];
+    for (int e2 = 0; e2 < E / 2; ++e2) {
+      f64x2 av[2], bv[2];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) cv[j] = cs[t][tx + 16 * j];
+      for (int r = 0; r < 2; ++r) av[r] = *(const f64x2*)(qstage + (ar0 + 16 * r) * RS + lk * E + 2 * e2);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int c = 0; c < 2; ++c) bv[c] = *(const f64x2*)(cstage + (bc0 + 16 * c) * RS + lk * E + 2 * e2);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fma(qv[i], cv[j], acc[i][j]);
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+            acc[r][c] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[r][h2], bv[c][h2], acc[r][c], 0, 0, 0);
     }
-    __syncthreads();
+    __syncthreads();  // the stage is read before the next chunk overwrites it
   }
 
+  if (hist_on) __syncthreads();  // the histogram is cleared
   const BucketMap bucket(a, bh, bkv);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int r = 0; r < 2; ++r)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (!(inr >> (4 * i + j) & 1)) continue;
-      const bool ok = adm >> (4 * i + j) & 1;
-      const double sv = ok ? acc[i][j] : SOC_NEG_INF;
-      out[(int64_t)(QB0 + ty + 16 * i) * a.nkb + KB0 + tx + 16 * j] = sv;
-      if (hist_on && ok) atomicAdd(&hist[bucket(sv)], 1u);
-    }
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int bit = (2 * r + c) * 4 + v;
+        if (!(inr >> bit & 1)) continue;
+        const bool ok = adm >> bit & 1;
+        const double sv = ok ? acc[r][c][v] : SOC_NEG_INF;
+        out_at(r, c, v) = sv;
+        if (hist_on && ok) atomicAdd(&hist[bucket(sv)], 1u);
+      }
   if (hist_on) {  // the tile's histogram as u16 pairs (a tile has at most 64*64 values)
     __syncthreads();
     constexpr int PER = kSelBuckets / NTHR;  // buckets per thread
@@ -379,38 +413,6 @@ __global__ void __launch_bounds__(NTHR) score_kernel(SelectArgs a) {
       dst[v] = w;
     }
   }
-}
-
-// Sums the per-tile histograms of each head into its value histogram (fixed tile order).
-// Grid: B * Hq * (kSelBuckets / 512); each thread owns a pair of buckets.
-__global__ void __launch_bounds__(NTHR) hist_reduce_kernel(SelectArgs a) {
-  constexpr int PARTS = kSelBuckets / (2 * NTHR);
-  const int part = blockIdx.x % PARTS;
-  const int64_t bh = blockIdx.x / PARTS;
-  const int64_t ntiles = (int64_t)((a.nqb + ST - 1) / ST) * ((a.nkb + ST - 1) / ST);
-  const int pair = part * NTHR + threadIdx.x;
-  const uint32_t* hp = a.hpart + bh * ntiles * (kSelBuckets / 2) + pair;
-  const uint32_t* fl = a.tflag + bh * ntiles;
-  uint32_t lo = 0, hi = 0;
-  int64_t t = 0;
-  for (; t + 8 <= ntiles; t += 8) {  // 8 tiles' loads in flight; tiles without data are masked
-    uint32_t w[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) w[u] = hp[(t + u) * (kSelBuckets / 2)];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const uint32_t m = fl[t + u] ? w[u] : 0u;
-      lo += m & 0xffffu;
-      hi += m >> 16;
-    }
-  }
-  for (; t < ntiles; ++t) {
-    const uint32_t m = fl[t] ? hp[t * (kSelBuckets / 2)] : 0u;
-    lo += m & 0xffffu;
-    hi += m >> 16;
-  }
-  a.hist[bh * kSelBuckets + 2 * pair] = lo;
-  a.hist[bh * kSelBuckets + 2 * pair + 1] = hi;
 }
 
 // Wave-wide search in descending value order.  Lane l holds the count c of the l-th of 64
@@ -434,19 +436,76 @@ __device__ int wave_locate_desc(unsigned long long c, unsigned long long target,
   return L;
 }
 
-constexpr int GCH = 32 * NTHR;  // score values scanned per gather workgroup
+// Per head: sums the tile histograms of its admissible s1 (fixed tile order), then finds the
+// bucket that holds descending rank n = floor(keep * N + 1/2) and the rank inside it; writes
+// (N, n, bucket or -1 when n >= N, rank) to pick.  One workgroup of 1024 threads per head,
+// thread t owning buckets 4t .. 4t+3.
+constexpr int PICK_THR = 1024;
+static_assert(kSelBuckets == 4 * PICK_THR, "four buckets per thread");
+__global__ void __launch_bounds__(PICK_THR) pick_kernel(SelectArgs a) {
+  __shared__ uint32_t hist[kSelBuckets];
+  const int64_t bh = blockIdx.x;
+  const int64_t ntiles = (int64_t)((a.nqb + ST - 1) / ST) * ((a.nkb + ST - 1) / ST);
+  const u32x2* hp = (const u32x2*)(a.hpart + bh * ntiles * (kSelBuckets / 2)) + threadIdx.x;
+  const uint32_t* fl = a.tflag + bh * ntiles;
+  uint32_t c4[4] = {0u, 0u, 0u, 0u};
+  auto add = [&](u32x2 w) __attribute__((always_inline)) {
+    c4[0] += w[0] & 0xffffu;
+    c4[1] += w[0] >> 16;
+    c4[2] += w[1] & 0xffffu;
+    c4[3] += w[1] >> 16;
+  };
+  int64_t t = 0;
+  for (; t + 8 <= ntiles; t += 8) {  // 8 tiles' loads in flight; tiles without data are masked
+    u32x2 w[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) w[u] = hp[(t + u) * (kSelBuckets / 4)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) add(fl[t + u] ? w[u] : u32x2{0u, 0u});
+  }
+  for (; t < ntiles; ++t) add(fl[t] ? hp[t * (kSelBuckets / 4)] : u32x2{0u, 0u});
+#pragma unroll
+  for (int e = 0; e < 4; ++e) hist[4 * threadIdx.x + e] = c4[e];
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    unsigned long long c = 0;
+#pragma unroll
+    for (int i = 0; i < 64; i += 4) {
+      const u32x4 w = *(const u32x4*)(hist + 64 * lane + i);
+      c += (unsigned long long)w[0] + w[1] + w[2] + w[3];
+    }
+    unsigned long long above1 = 0, N = 0;
+    wave_locate_desc(c, 0, &above1, &N);  // N only
+    const double nd = floor(a.keep_mean * (double)N + 0.5);
+    long long sel[4] = {(long long)N, (long long)nd, -1, 0};
+    if (nd < (double)N) {
+      const unsigned long long n = (unsigned long long)nd;
+      const int L1 = wave_locate_desc(c, n, &above1, &N);
+      unsigned long long above2 = 0, n1 = 0;
+      const int L2 = wave_locate_desc(hist[64 * L1 + lane], n - above1, &above2, &n1);
+      sel[2] = 64 * L1 + L2;
+      sel[3] = (long long)(n - above1 - above2);
+    }
+    if (lane < 4) a.pick[bh * 4 + lane] = sel[lane];
+  }
+}
 
-// Finds, per head, the histogram bucket that holds descending rank n of the admissible s1 and
-// appends every s1 of that bucket to the head's candidate list.  Every workgroup of a head
-// locates the bucket itself (a 16 KB read); the first records it for threshold_kernel.
+constexpr int GCH = kSelGatherChunk;  // score values scanned per gather workgroup
+static_assert(GCH % NTHR == 0, "whole values per thread");
+
+// Copies every s1 of the head's picked bucket (typically a few dozen values) into this
+// workgroup's own segment of the candidate array (cand[bh][chunk][...], count in
+// ccount[bh][chunk]): a streaming filter over the scores with no atomics.
 __global__ void __launch_bounds__(NTHR) gather_kernel(SelectArgs a) {
-  __shared__ long long sel[4];  // N, n, bucket (-1: nothing to gather), rank within bucket
+  __shared__ int wcount[NTHR / 64];
   const int64_t P = (int64_t)a.nqb * a.nkb;
   const int nch = (int)((P + GCH - 1) / GCH);
   const int ch = blockIdx.x % nch;
   const int64_t bh = blockIdx.x / nch;
-  const int lane = threadIdx.x & 63;
-  // this workgroup's slice of the head's s1, loaded before the bucket search so the two overlap
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const long long beta = a.pick[bh * 4 + 2];
+  if (beta < 0) return;
   const double* sc = a.score + bh * P;
   const int64_t i0 = (int64_t)ch * GCH;
   double sv[GCH / NTHR];
@@ -455,71 +514,46 @@ __global__ void __launch_bounds__(NTHR) gather_kernel(SelectArgs a) {
     const int64_t i = i0 + r * NTHR + threadIdx.x;
     sv[r] = i < P ? sc[i] : SOC_NEG_INF;
   }
-  if (threadIdx.x < 64) {
-    const uint32_t* hh = a.hist + bh * kSelBuckets;
-    unsigned long long c = 0;
-#pragma unroll
-    for (int i = 0; i < 64; i += 4) {
-      const u32x4 w = *(const u32x4*)(hh + 64 * lane + i);
-      c += (unsigned long long)w[0] + w[1] + w[2] + w[3];
-    }
-    unsigned long long above1 = 0, N = 0;
-    int L1 = wave_locate_desc(c, 0, &above1, &N);  // N only; L1 recomputed below
-    const double nd = floor(a.keep_mean * (double)N + 0.5);
-    if (nd >= (double)N) {
-      if (lane == 0) {
-        sel[0] = (long long)N;
-        sel[1] = (long long)nd;
-        sel[2] = -1;
-        sel[3] = 0;
-      }
-    } else {
-      const unsigned long long n = (unsigned long long)nd;
-      L1 = wave_locate_desc(c, n, &above1, &N);
-      unsigned long long above2 = 0, n1 = 0;
-      const int L2 = wave_locate_desc(hh[64 * L1 + lane], n - above1, &above2, &n1);
-      if (lane == 0) {
-        sel[0] = (long long)N;
-        sel[1] = (long long)n;
-        sel[2] = 64 * L1 + L2;
-        sel[3] = (long long)(n - above1 - above2);
-      }
-    }
-  }
-  __syncthreads();
-  if (ch == 0 && threadIdx.x < 4) a.pick[bh * 4 + threadIdx.x] = sel[threadIdx.x];
-  const long long beta = sel[2];
-  if (beta < 0) return;
   const BucketMap bucket(a, bh, (int64_t)(bh / a.Hq) * a.Hkv + (bh % a.Hq) / a.g);
-  double* cd = a.cand + bh * P;
+  unsigned long long bal[GCH / NTHR];
+  int n = 0;
 #pragma unroll
-  for (int r = 0; r < GCH / NTHR; ++r) {  // same trip count in every lane
-    const double v = sv[r];
-    const bool m = v > SOC_NEG_INF && bucket(v) == (int)beta;
-    const unsigned long long bal = __ballot(m);
-    if (bal) {
-      unsigned slot = 0;
-      if (lane == 0) slot = atomicAdd(&a.ccount[bh], (unsigned)__popcll(bal));
-      slot = __shfl(slot, 0, 64);
-      if (m) cd[slot + __popcll(bal & ((1ull << lane) - 1ull))] = v;
-    }
+  for (int r = 0; r < GCH / NTHR; ++r) {
+    bal[r] = __ballot(sv[r] > SOC_NEG_INF && bucket(sv[r]) == (int)beta);
+    n += __popcll(bal[r]);
   }
+  if (lane == 0) wcount[wave] = n;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += wcount[w];
+  double* cd = a.cand + bh * P + i0;
+#pragma unroll
+  for (int r = 0; r < GCH / NTHR; ++r) {
+    if (bal[r] >> lane & 1) cd[base + __popcll(bal[r] & ((1ull << lane) - 1ull))] = sv[r];
+    base += __popcll(bal[r]);
+  }
+  if (threadIdx.x == NTHR - 1) a.ccount[bh * nch + ch] = base;  // the last wave's base is the total
 }
 
-// Exact value at descending rank `rank` (0 = largest) among the finite values of vals[0,
-// count): 8 passes of an 8-bit radix select on order-preserving keys, 1024 threads.
-__device__ double select_desc(const double* vals, int64_t count, unsigned long long rank, unsigned* hist,
-                              unsigned long long* su) {
+// Exact value at descending rank `rank` (0 = largest) among the finite values of nseg
+// segments: vals[s * seg_len + i] for i < counts[s] (one segment when counts is null, count
+// values).  8 passes of an 8-bit radix select on order-preserving keys, 1024 threads.
+__device__ double select_desc(const double* vals, int64_t count, const unsigned* counts, int nseg, int64_t seg_len,
+                              unsigned long long rank, unsigned* hist, unsigned long long* su) {
   constexpr int T = 1024;
   unsigned long long prefix = 0, pmask = 0;
   for (int shift = 56; shift >= 0; shift -= 8) {
     for (int i = threadIdx.x; i < 256; i += T) hist[i] = 0;
     __syncthreads();
-    for (int64_t i = threadIdx.x; i < count; i += T) {
-      const double x = vals[i];
-      if (!(x > SOC_NEG_INF)) continue;
-      const uint64_t key = f64_order_key(x);
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    for (int sg = 0; sg < (counts ? nseg : 1); ++sg) {
+      const int64_t cnt = counts ? (int64_t)counts[sg] : count;
+      const double* v = vals + sg * seg_len;
+      for (int64_t i = threadIdx.x; i < cnt; i += T) {
+        const double x = v[i];
+        if (!(x > SOC_NEG_INF)) continue;
+        const uint64_t key = f64_order_key(x);
+        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      }
     }
     __syncthreads();
     if (threadIdx.x < 64) {  // wave 0 picks the digit: lane l covers digits 4l..4l+3
@@ -549,16 +583,55 @@ __device__ double select_desc(const double* vals, int64_t count, unsigned long l
   return f64_from_order_key(prefix);
 }
 
+constexpr int CAND_LDS = 2048;  // candidates selected in LDS (more: straight from their segments)
+
 __global__ void __launch_bounds__(1024) threshold_kernel(SelectArgs a) {
   __shared__ unsigned hist[256];
   __shared__ unsigned long long su[2];
+  __shared__ unsigned seg_end[64];
+  __shared__ double cv[CAND_LDS];
   const int nmean = a.keep_mean >= 0.0 ? a.B * a.Hq : 0;
   int id = blockIdx.x;
   if (id < nmean) {
     const int64_t* pk = a.pick + (int64_t)id * 4;
     double tau = SOC_NEG_INF;
-    if (pk[2] >= 0)
-      tau = select_desc(a.cand + (int64_t)id * a.nqb * a.nkb, a.ccount[id], (unsigned long long)pk[3], hist, su);
+    const int64_t P = (int64_t)a.nqb * a.nkb;
+    const int nch = (int)((P + GCH - 1) / GCH);
+    const double* cand = a.cand + (int64_t)id * P;
+    const unsigned* cnt = a.ccount + (int64_t)id * nch;
+    if (pk[2] >= 0) {
+      // the candidates of all gather chunks, contiguous in LDS when they fit
+      unsigned total = 0;
+      if (threadIdx.x < 64) {  // inclusive prefix of the chunk counts, 64 chunks per pass
+        unsigned run = 0;
+        for (int c0 = 0; c0 < nch; c0 += 64) {
+          const unsigned x = c0 + (int)threadIdx.x < nch ? cnt[c0 + threadIdx.x] : 0u;
+          unsigned incl = x;
+#pragma unroll
+          for (int o = 1; o < 64; o <<= 1) {
+            const unsigned y = __shfl_up(incl, o, 64);
+            if ((int)threadIdx.x >= o) incl += y;
+          }
+          if (nch <= 64) seg_end[threadIdx.x] = run + incl;
+          run += __shfl(incl, 63, 64);
+        }
+        if (threadIdx.x == 0) su[0] = run;
+      }
+      __syncthreads();
+      total = (unsigned)su[0];
+      __syncthreads();
+      if (nch <= 64 && total <= (unsigned)CAND_LDS) {
+        for (unsigned i = threadIdx.x; i < total; i += 1024) {
+          int sg = 0;
+          while (seg_end[sg] <= i) ++sg;
+          cv[i] = cand[(int64_t)sg * GCH + (i - (sg ? seg_end[sg - 1] : 0u))];
+        }
+        __syncthreads();
+        tau = select_desc(cv, total, nullptr, 1, 0, (unsigned long long)pk[3], hist, su);
+      } else {
+        tau = select_desc(cand, 0, cnt, nch, GCH, (unsigned long long)pk[3], hist, su);
+      }
+    }
     if (threadIdx.x == 0) a.tau_mean[id] = tau;
   } else {
     id -= nmean;
@@ -572,7 +645,7 @@ __global__ void __launch_bounds__(1024) threshold_kernel(SelectArgs a) {
     const unsigned long long N = su[0];
     __syncthreads();
     const double nd = floor(a.keep_radius * (double)N + 0.5);
-    const double tau = nd >= (double)N ? SOC_NEG_INF : select_desc(vals, a.nkb, (unsigned long long)nd, hist, su);
+    const double tau = nd >= (double)N ? SOC_NEG_INF : select_desc(vals, a.nkb, nullptr, 1, 0, (unsigned long long)nd, hist, su);
     if (threadIdx.x == 0) a.tau_radius[id] = tau;
   }
 }
@@ -601,20 +674,36 @@ __device__ void compact_row(int n_kb, KeepFn keep, uint8_t* mask_row, int32_t* l
   if (threadIdx.x == 0 && list_row) list_row[0] = base;
 }
 
+// One wave per (b, h, query block) row: the mask bytes and the ascending kept list, 64 key
+// blocks per step with a ballot (no barriers).
 __global__ void __launch_bounds__(NTHR) mask_kernel(SelectArgs a) {
-  __shared__ int wsum[4];
-  const int qb = blockIdx.x % a.nqb;
-  const int h = (blockIdx.x / a.nqb) % a.Hq;
-  const int b = blockIdx.x / (a.nqb * a.Hq);
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * (NTHR / 64) + (threadIdx.x >> 6);
+  const int64_t rows = (int64_t)a.B * a.Hq * a.nqb;
+  if (row >= rows) return;
+  const int h = (int)((row / a.nqb) % a.Hq);
+  const int b = (int)(row / ((int64_t)a.nqb * a.Hq));
   const int kvh = h / a.g;
-  const int64_t row = ((int64_t)b * a.Hq + h) * a.nqb + qb;
   const double* sc = a.score + row * a.nkb;
   const double* r2 = a.rad2 + ((int64_t)b * a.Hkv + kvh) * a.nkb;
   const double t1 = a.tau_mean[b * a.Hq + h];
   const double t2 = a.tau_radius[b * a.Hkv + kvh];
-  compact_row(
-      a.nkb, [&](int kb) { const double s = sc[kb]; return s > SOC_NEG_INF && (s > t1 || r2[kb] > t2); },
-      a.mask + row * a.nkb, a.list ? a.list + row * (1 + a.nkb) : nullptr, wsum);
+  uint8_t* mrow = a.mask + row * a.nkb;
+  int32_t* lrow = a.list ? a.list + row * (1 + a.nkb) : nullptr;
+  int base = 0;
+  for (int k0 = 0; k0 < a.nkb; k0 += 64) {
+    const int kb = k0 + lane;
+    bool kept = false;
+    if (kb < a.nkb) {
+      const double sv = sc[kb];
+      kept = sv > SOC_NEG_INF && (sv > t1 || r2[kb] > t2);
+      mrow[kb] = kept ? 1 : 0;
+    }
+    const unsigned long long bal = __ballot(kept);
+    if (kept && lrow) lrow[1 + base + __popcll(bal & ((1ull << lane) - 1ull))] = kb;
+    base += __popcll(bal);
+  }
+  if (lane == 0 && lrow) lrow[0] = base;
 }
 
 __global__ void __launch_bounds__(NTHR) list_from_mask_kernel(int32_t n_kb, const uint8_t* mask, int32_t* list) {
@@ -630,20 +719,19 @@ hipError_t launch_select_d(const SelectArgs& a, hipStream_t s) {
   const unsigned gk = (unsigned)((int64_t)a.B * a.Hkv * a.nkb);
   const bool mean_on = a.keep_mean >= 0.0;
   const int64_t bh = (int64_t)a.B * a.Hq;
-  hipLaunchKernelGGL((qmean_kernel<T, D>), dim3(gq), dim3(NTHR), 0, s, a);
-  hipLaunchKernelGGL((kstats_kernel<T, D>), dim3(gk), dim3(NTHR), 0, s, a);
+  hipLaunchKernelGGL((stats_kernel<T, D>), dim3(gq + gk), dim3(NTHR), 0, s, a);
   if (mean_on)
     hipLaunchKernelGGL(norm_max_kernel, dim3((unsigned)(bh + (int64_t)a.B * a.Hkv)), dim3(NTHR), 0, s, a);
   const int64_t ntq = (a.nqb + ST - 1) / ST, ntk = (a.nkb + ST - 1) / ST;
   hipLaunchKernelGGL(score_kernel<D>, dim3((unsigned)(bh * ntq * ntk)), dim3(NTHR), 0, s, a);
   if (mean_on) {
-    hipLaunchKernelGGL(hist_reduce_kernel, dim3((unsigned)(bh * (kSelBuckets / (2 * NTHR)))), dim3(NTHR), 0, s, a);
+    hipLaunchKernelGGL(pick_kernel, dim3((unsigned)bh), dim3(PICK_THR), 0, s, a);
     const int64_t nch = ((int64_t)a.nqb * a.nkb + GCH - 1) / GCH;
     hipLaunchKernelGGL(gather_kernel, dim3((unsigned)(bh * nch)), dim3(NTHR), 0, s, a);
   }
   const unsigned gt = (mean_on ? a.B * a.Hq : 0) + (a.keep_radius >= 0.0 ? a.B * a.Hkv : 0);
   if (gt) hipLaunchKernelGGL(threshold_kernel, dim3(gt), dim3(1024), 0, s, a);
-  hipLaunchKernelGGL(mask_kernel, dim3(gq), dim3(NTHR), 0, s, a);
+  hipLaunchKernelGGL(mask_kernel, dim3((gq + NTHR / 64 - 1) / (NTHR / 64)), dim3(NTHR), 0, s, a);
   return hipGetLastError();
 }
 

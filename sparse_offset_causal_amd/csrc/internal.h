@@ -59,6 +59,7 @@ __host__ __device__ inline size_t decode_ml_floats(const AttnArgs& a) { return d
 // the square tile of (query block, key block) scores one workgroup computes.
 constexpr int kSelBuckets = 4096;
 constexpr int kScoreTile = 64;
+constexpr int kSelGatherChunk = 8192;  // scores one candidate-gather workgroup scans
 
 struct SelectArgs {
   const void* q;
@@ -74,15 +75,14 @@ struct SelectArgs {
   uint8_t* mask;       // [B, Hq, nqb, nkb]
   int32_t* list;       // [B, Hq, nqb, 1 + nkb] or null
   double* qmean;       // workspace [B, Hq, nqb, d]
-  double* cT;          // workspace [B, Hkv, d, nkb]
+  double* cent;        // workspace [B, Hkv, nkb, d]  key-block centroids
   double* rad2;        // workspace [B, Hkv, nkb]
   double* score;       // workspace [B, Hq, nqb, nkb]
   double* norm2;       // workspace [B, Hq, nqb] |qmean|^2 then [B, Hkv, nkb] |c|^2
   double* nmax;        // workspace [B*Hq] max |qmean|^2 per head, then [B*Hkv] max |c|^2
   uint32_t* hpart;     // workspace [B, Hq, score tiles, kSelBuckets / 2]  per-tile histograms (u16 pairs)
   uint32_t* tflag;     // workspace [B, Hq, score tiles]  1 if the tile holds an admissible pair
-  uint32_t* hist;      // workspace [B, Hq, kSelBuckets]  value histogram of the admissible s1
-  uint32_t* ccount;    // workspace [B, Hq]  candidates gathered
+  uint32_t* ccount;    // workspace [B, Hq, gather chunks]  candidates gathered per chunk
   int64_t* pick;       // workspace [B, Hq, 4]  (N, n, bucket, rank within bucket)
   double* cand;        // workspace [B, Hq, nqb * nkb]  candidates of the order statistic
 };
