@@ -41,7 +41,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 import synth  # noqa: E402
-from sparse_offset_causal_amd import (attn_block_select, attn_decode, attn_decode_workspace_bytes,  # noqa: E402
+from sparse_offset_causal_amd import (attn_block_select, attn_block_select_workspace_bytes,  # noqa: E402
+                                      attn_block_sparse_prefill, attn_decode, attn_decode_workspace_bytes,
                                       attn_dsa_decode, attn_dsa_decode_workspace_bytes, attn_mla_decode, attn_mla_decode_workspace_bytes, attn_prefill,
                                       attn_ring_decode, attn_ring_decode_workspace_bytes)
 
@@ -108,6 +109,31 @@ class Timer:
                     call_ms_median=float(np.median(per)), call_ms_min=float(np.min(per)))
 
 
+class OracleClock:
+    """Times the float64 oracle on the host on a bounded sample of a workload: `units` are
+    callables (one sampled piece of the workload each) run in order until `budget_s` has
+    passed; `work` gives each piece's algorithmic work (flops or bytes, as the GPU line
+    counts them).  Reported as a rate in the GPU line's unit, with the host threads used."""
+
+    enabled = True
+    cores = 1
+
+    @classmethod
+    def run(cls, units, work, scale, unit, what, budget_s=3.0):
+        if not cls.enabled:
+            return None
+        done, w, t0 = 0, 0.0, time.perf_counter()
+        for fn, wk in zip(units, work):
+            fn()
+            done += 1
+            w += wk
+            if time.perf_counter() - t0 > budget_s:
+                break
+        dt = time.perf_counter() - t0
+        return {"value": w / dt / scale, "unit": unit, "cores": cls.cores, "kind": "oracle",
+                "sample": f"{done} {what} (float64 numpy/BLAS), {dt:.1f} s"}
+
+
 def to_dev(w):
     f = lambda t: None if t is None else t.to("cuda", non_blocking=False)
     return f(w.q), f(w.k), f(w.v), f(w.cache_off), f(w.sink)
@@ -135,6 +161,13 @@ def bench_window_sink(steps, warmup, T=32768, W=1024):
     flops = prefill_flops(32, 128, allowed_pairs(T, T, W))
     r.update(workload=w.name, flops_per_step=flops, value=flops / (r["ms_per_step"] * 1e-3) / 1e12,
              kernel_tflops=flops / (r["gpu_ms_per_step"] * 1e-3) / 1e12, unit="TFLOP/s")
+    from oracle import attend
+    rows = np.arange(T // 2, T // 2 + 1024)  # 1024 rows past the window's start, one head at a time
+    pairs = float(sum(min(W, int(p) + 1) for p in rows))
+    units = [lambda h=h: attend(w.q, w.k, w.v, cache_off=[0], window=W, sink=w.sink, rows=rows, heads=[h])
+             for h in range(32)]
+    r["cpu_baseline"] = OracleClock.run(units, [4.0 * 128 * pairs] * 32, 1e12, "TFLOP/s",
+                                        "heads x 1024 rows of the window workload")
     return r
 
 
@@ -165,8 +198,67 @@ def bench_decode_and_chunk(steps, warmup, B=64):
     rc.update(workload=f"chunk512_bf16_B{B}_cache1024-32768_{Hq}q{Hkv}kv_d{d}", flops_per_step=flops,
               value=flops / (rc["ms_per_step"] * 1e-3) / 1e12, kernel_tflops=flops / (rc["gpu_ms_per_step"] * 1e-3) / 1e12,
               unit="TFLOP/s")
+    from oracle import attend
+    sl = lambda t, b: t[b:b + 1]
+    units = [lambda b=b: attend(sl(c.q_decode, b), sl(c.k, b), sl(c.v, b), cache_off=[int(L[b])]) for b in range(B)]
+    work = [float(2 * Hkv * (L[b] + 1) * d * 2 + 2 * Hq * d * 2) for b in range(B)]
+    rd["cpu_baseline"] = OracleClock.run(units, work, 1e9, "GB/s", "sequences (all 32 heads) of the decode step")
+    units = [lambda b=b: attend(sl(c.q_chunk, b), sl(c.k, b), sl(c.v, b), cache_off=[int(L[b])], heads=[0, 11, 22])
+             for b in range(B)]
+    work = [prefill_flops(3, d, allowed_pairs(c.chunk, int(L[b]) + c.chunk, 0)) for b in range(B)]
+    rc["cpu_baseline"] = OracleClock.run(units, work, 1e12, "TFLOP/s", "sequences x 3 heads of the 512-row chunk")
+    rcs = bench_chunk_block_sparse(c, k, v, off, steps, warmup)
     del k, v
-    return rd, rc
+    return rd, rc, rcs
+
+
+def bench_chunk_block_sparse(c, k, v, off, steps, warmup, BS=128, keep=0.05):
+    """The 512-token chunk at every sequence's cache offset with query-chunked block selection
+    (keep fractions 0.05 / 0.05) fused into the prefill: selection + prefill in one call."""
+    B, Hq, d = c.q_chunk.shape[0], 32, 128
+    qc = c.q_chunk.to("cuda")
+    oc = torch.empty_like(qc)
+    ws = torch.empty(attn_block_select_workspace_bytes(qc, k, BS), dtype=torch.uint8, device="cuda")
+    tm = torch.empty((B, Hq), dtype=torch.float64, device="cuda")
+    tr = torch.empty((B, 8), dtype=torch.float64, device="cuda")
+    fn = lambda: attn_block_sparse_prefill(qc, k, v, cache_off=off, keep_mean=keep, keep_radius=keep, tau_mean=tm,
+                                           tau_radius=tr, workspace=ws, out=oc)
+    r = Timer(fn, max(3, steps // 2), max(1, warmup // 2)).run()
+    sel = attn_block_select(qc, k, block_size=BS, cache_off=off, keep_mean=keep, keep_radius=keep)
+    L = c.lengths.numpy().astype(np.int64)
+    mask = sel["mask"].to(torch.int64).cpu().numpy()
+    pairs = 0
+    for b in range(B):  # allowed (row, key) pairs inside the kept blocks
+        off_b = int(L[b])
+        for qb in range(mask.shape[2]):
+            r0, r1 = qb * BS, min((qb + 1) * BS, c.chunk)
+            pos = np.arange(off_b + r0, off_b + r1)
+            kbs = np.nonzero(mask[b, :, qb].sum(0))[0]
+            for kb in kbs:
+                j0, j1 = kb * BS, (kb + 1) * BS
+                per_row = np.clip(np.minimum(pos + 1, j1) - j0, 0, None)
+                pairs += int(mask[b, :, qb, kb].sum()) * int(per_row.sum())
+    flops = 4.0 * d * pairs
+    sel_bytes = float(qc.numel() * 2 + sum(8 * (int(l) + c.chunk) * d * 2 for l in L))
+    r.update(workload=f"chunk512_block_sparse_bf16_B{B}_cache1024-32768_32q8kv_d128_keep{keep}", flops_per_step=flops,
+             value=flops / (r["ms_per_step"] * 1e-3) / 1e12, kernel_tflops=flops / (r["gpu_ms_per_step"] * 1e-3) / 1e12,
+             unit="TFLOP/s (kept pairs; selection included in the time)",
+             kept_fraction=float(mask.sum()) / float(sum(Hq * sum((int(l) + min((qb + 1) * BS, c.chunk) - 1) // BS + 1
+                                                             for qb in range(mask.shape[2])) for l in L)),
+             select_bytes=sel_bytes)
+    from oracle import attend, select_blocks
+    sl = lambda t, b: t[b:b + 1]
+
+    def unit(b):
+        m = select_blocks(sl(c.q_chunk, b), sl(c.k, b), BS, cache_off=[int(L[b])], keep_mean=keep, keep_radius=keep)
+        attend(sl(c.q_chunk, b), sl(c.k, b), sl(c.v, b), cache_off=[int(L[b])], heads=[0, 11, 22],
+               block_mask=m["mask"], block_size=BS)
+
+    work = [flops / B * 3 / Hq] * B  # the mean kept work of a sequence's three heads
+    r["cpu_baseline"] = OracleClock.run([lambda b=b: unit(b) for b in range(B)], work, 1e12, "TFLOP/s",
+                                        "sequences: selection (all heads) + 3 heads' block-sparse chunk")
+    del qc
+    return r
 
 
 def bench_ring_decode(steps, warmup, B=64, W=1024):
@@ -186,6 +278,17 @@ def bench_ring_decode(steps, warmup, B=64, W=1024):
     r.update(workload=f"ring_decode_bf16_B{B}_W{W}_{Hq}q{Hkv}kv_d{d}", bytes_per_step=nbytes,
              value=nbytes / (r["ms_per_step"] * 1e-3) / 1e9, kernel_GBps=nbytes / (r["gpu_ms_per_step"] * 1e-3) / 1e9,
              unit="GB/s")
+    from oracle.ring import RingCache, attend_unmasked
+    qh, knh, vnh = (t.cpu() for t in synth.ring_step(B, Hq, Hkv, d, 0))
+
+    def unit(b):
+        rc = RingCache(Hkv, d, W)
+        rc.k, rc.v, rc.n = st.k[b].double().numpy(), st.v[b].double().numpy(), int(st.n_seen[b])
+        K, V = rc.add(knh[b, :, 0].double().numpy(), vnh[b, :, 0].double().numpy())
+        attend_unmasked(qh[b, :, 0].double().numpy(), K, V, Hq, sink=st.sink.double().numpy())
+
+    r["cpu_baseline"] = OracleClock.run([lambda b=b: unit(b) for b in range(B)], [nbytes / B] * B, 1e9, "GB/s",
+                                        "sequences (all heads) of the ring step", budget_s=2.0)
     return r
 
 
@@ -207,6 +310,12 @@ def bench_mla_decode(steps, warmup, B=64, H=16):
              value=nbytes / (r["ms_per_step"] * 1e-3) / 1e9, kernel_GBps=nbytes / (r["gpu_ms_per_step"] * 1e-3) / 1e9,
              unit="GB/s")
     del ck, kr
+    from oracle.mla import mla_absorbed
+    sl = lambda t, b: t[b:b + 1]
+    units = [lambda b=b: mla_absorbed(sl(m.q_nope, b), sl(m.q_rope, b), sl(m.c_kv, b), sl(m.k_rope, b), m.w_uk, m.w_uv,
+                                      cache_off=sl(m.cache_off, b)) for b in range(B)]
+    work = [float((L[b] + 1) * (512 + 64) * 2) for b in range(B)]
+    r["cpu_baseline"] = OracleClock.run(units, work, 1e9, "GB/s", "sequences (all heads) of the MLA step", budget_s=2.0)
     return r
 
 
@@ -230,10 +339,20 @@ def bench_dsa_decode(steps, warmup, B=64, topk=2048):
              bytes_per_step=nbytes, value=nbytes / (r["ms_per_step"] * 1e-3) / 1e9,
              kernel_GBps=nbytes / (r["gpu_ms_per_step"] * 1e-3) / 1e9, unit="GB/s")
     del k, v
+    from oracle.dsa import sparse_attend
+    sl = lambda t, b: t[b:b + 1]
+    units = [lambda b=b: sparse_attend(sl(x.q, b), sl(x.k, b), sl(x.v, b), sl(x.qi, b), sl(x.ki, b), sl(x.wi, b), topk,
+                                       cache_off=sl(x.cache_off, b), sink=x.sink) for b in range(B)]
+    work = [float(L[b] * 128 * 2 + 2 * Hkv * min(L[b], topk) * d * 2) for b in range(B)]
+    r["cpu_baseline"] = OracleClock.run(units, work, 1e9, "GB/s", "sequences (indexer, top-k, all heads) of the step",
+                                        budget_s=2.0)
     return r
 
 
 def bench_block_sparse(steps, warmup, T=65536, BS=128):
+    """Block selection and block-sparse prefill at T = 65536: the selection alone, the prefill
+    alone over the selection's kept lists, and the two in one call (the prefill deciding each
+    key block from the selection's scores and thresholds)."""
     w = synth.block_sparse_prefill(T=T, BS=BS)
     q, k, v, _, _ = to_dev(w)
     sel_fn = lambda: attn_block_select(q, k, block_size=BS, keep_mean=w.keep_mean, keep_radius=w.keep_radius)
@@ -242,6 +361,12 @@ def bench_block_sparse(steps, warmup, T=65536, BS=128):
     out = torch.empty_like(q)
     fn = lambda: attn_prefill(q, k, v, block_list=sel["list"], block_size=BS, out=out)
     rp = Timer(fn, max(3, steps // 2), max(1, warmup // 2)).run()
+    ws = torch.empty(attn_block_select_workspace_bytes(q, k, BS), dtype=torch.uint8, device="cuda")
+    tm = torch.empty((1, 32), dtype=torch.float64, device="cuda")
+    tr = torch.empty((1, 8), dtype=torch.float64, device="cuda")
+    ffn = lambda: attn_block_sparse_prefill(q, k, v, keep_mean=w.keep_mean, keep_radius=w.keep_radius, tau_mean=tm,
+                                            tau_radius=tr, workspace=ws, out=out)
+    rf = Timer(ffn, max(3, steps // 2), max(1, warmup // 2)).run()
     m = sel["mask"].to(torch.int64)
     nb = T // BS
     diag = int(torch.diagonal(m, dim1=-2, dim2=-1).sum())
@@ -256,31 +381,40 @@ def bench_block_sparse(steps, warmup, T=65536, BS=128):
     rs.update(workload=f"block_select_fp64_T{T}_BS{BS}_32q8kv_d128", bytes_per_step=sel_bytes,
               value=sel_bytes / (rs["ms_per_step"] * 1e-3) / 1e9, unit="GB/s (q+k read)")
     rp["select_plus_prefill_ms"] = rs["ms_per_step"] + rp["ms_per_step"]
+    rp["fused_select_prefill_ms"] = rf["ms_per_step"]
+    rp["fused_select_prefill_gpu_ms"] = rf["gpu_ms_per_step"]
+    from oracle import attend
+    mask_h = sel["mask"].cpu().numpy()
+    qbs = [64, 200, 300, 420, 511]  # query blocks (128 rows) of head 0 .. 4, one each
+
+    def unit(i):
+        h = i % 32
+        rows = np.arange(qbs[i % 5] * BS, qbs[i % 5] * BS + BS)
+        attend(w.q, w.k, w.v, rows=rows, heads=[h], block_mask=mask_h, block_size=BS)
+
+    def unit_work(i):
+        h, qb = i % 32, qbs[i % 5]
+        kept = mask_h[0, h, qb]
+        return 4.0 * 128 * (int(kept[:qb].sum()) * BS * BS + int(kept[qb]) * BS * (BS + 1) // 2)
+
+    n = 64
+    rp["cpu_baseline"] = OracleClock.run([lambda i=i: unit(i) for i in range(n)], [unit_work(i) for i in range(n)], 1e12,
+                                         "TFLOP/s", "(head, 128-row query block) pieces of the block-sparse prefill")
     return rs, rp
 
 
 # ------------------------------------------------------------------ CPU baseline
-def cpu_baseline(w, budget_s=15.0):
+def cpu_baseline(w, budget_s=12.0):
     """The float64 oracle on host cores on a bounded sample of the causal-prefill workload:
     whole heads (all 8192 rows) until the time budget is spent; value in TFLOP/s of the
     same algorithmic flops."""
-    from threadpoolctl import threadpool_info
-
     from oracle import attend
 
     T = w.q.shape[2]
-    heads_done, t0 = 0, time.perf_counter()
     q, k, v = w.q.double().numpy(), w.k.double().numpy(), w.v.double().numpy()
-    for h in range(w.q.shape[1]):
-        attend(q, k, v, cache_off=[0], scale=w.scale, heads=[h])
-        heads_done += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
-    dt = time.perf_counter() - t0
-    flops = 4.0 * 128 * heads_done * allowed_pairs(T, T, 0)
-    threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{heads_done} of 32 query heads, all {T} rows each (float64 numpy/BLAS), {dt:.1f} s"}
+    units = [lambda h=h: attend(q, k, v, cache_off=[0], scale=w.scale, heads=[h]) for h in range(w.q.shape[1])]
+    work = [4.0 * 128 * allowed_pairs(T, T, 0)] * w.q.shape[1]
+    return OracleClock.run(units, work, 1e12, "TFLOP/s", f"of 32 query heads, all {T} rows each", budget_s=budget_s)
 
 
 # ------------------------------------------------------------------ measured traffic
@@ -312,7 +446,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", default="all",
-                    help="all | causal_prefill | window_sink | decode | ring_decode | mla_decode | dsa_decode | block_sparse | "
+                    help="all | causal_prefill | window_sink | decode (with the chunk and its block-sparse form) | ring_decode | "
+                         "mla_decode | dsa_decode | block_sparse | "
                          "copy (HBM counter calibration)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -326,6 +461,13 @@ def main():
         sys.exit(2)
     torch.cuda.set_device(0)
     torch.backends.cuda.matmul.allow_tf32 = False
+    # the oracle's host timing uses every core this process may run on, BLAS threads to match
+    from threadpoolctl import threadpool_limits
+
+    OracleClock.cores = len(os.sched_getaffinity(0))
+    OracleClock.enabled = not args.no_cpu_baseline
+    threadpool_limits(limits=OracleClock.cores, user_api="blas")
+    torch.set_num_threads(OracleClock.cores)
 
     def log(msg):
         print(msg, file=sys.stderr, flush=True)
@@ -353,9 +495,10 @@ def main():
         log(f"window+sink prefill: {r['value']:.1f} TFLOP/s ({r['ms_per_step']:.3f} ms)")
         torch.cuda.empty_cache()
     if args.only in ("all", "decode"):
-        rd, rc = bench_decode_and_chunk(args.steps, args.warmup)
-        also["decode"], also["chunk_prefill"] = rd, rc
-        log(f"decode: {rd['value']:.0f} GB/s ({rd['ms_per_step']:.3f} ms); chunk: {rc['value']:.1f} TFLOP/s")
+        rd, rc, rcs = bench_decode_and_chunk(args.steps, args.warmup)
+        also["decode"], also["chunk_prefill"], also["chunk_block_sparse"] = rd, rc, rcs
+        log(f"decode: {rd['value']:.0f} GB/s ({rd['ms_per_step']:.3f} ms); chunk: {rc['value']:.1f} TFLOP/s; "
+            f"chunk block-sparse (selection included): {rcs['ms_per_step']:.3f} ms, kept {rcs['kept_fraction']:.3f}")
         torch.cuda.empty_cache()
     if args.only in ("all", "ring_decode"):
         r = bench_ring_decode(args.steps, args.warmup)

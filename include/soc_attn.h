@@ -318,6 +318,37 @@ int attn_block_select(const attn_shape_t* shape, const void* q, attn_strides_t q
                       hipStream_t stream);
 
 /*
+ * attn_block_sparse_prefill_workspace_bytes -- device workspace attn_block_sparse_prefill needs
+ * (the block selection's); 0 for an invalid shape.
+ */
+size_t attn_block_sparse_prefill_workspace_bytes(const attn_shape_t* shape, int32_t block_size);
+
+/*
+ * attn_block_sparse_prefill -- block selection and block-sparse prefill in one call (patty.io
+ * RBS-Attention review: the mean-centroid and max-radius sieves chosen per prompt and head, and
+ * the regular block-sparse execution they feed, section on how regular sparsity persuades the
+ * GPU).  Computes exactly attn_block_select's mask followed by attn_prefill over it, but the
+ * prefill decides each key block itself from the selection's fp64 scores, squared radii and
+ * thresholds held in the workspace (kept iff admissible and (s1 > tau_mean or rad2 >
+ * tau_radius)): no mask or kept list is written or read between the two.  With a cache offset
+ * this is the query-chunked selection of a chunked prefill: query block qb covers rows
+ * [qb*bs, (qb+1)*bs) of the tq-row chunk, key blocks are absolute.
+ *  q, k, v, o, cache_off, window, sink, scale: as attn_prefill (bf16: head_dim 128).
+ *  block_size, keep_mean, keep_radius, tau_mean, tau_radius: as attn_block_select (bf16:
+ *             block_size 128); the thresholds are written (or read, with a negative keep
+ *             fraction) as there.
+ *  block_mask_out  NULL, or device uint8 [batch, n_heads, nQB, nKB] to receive the mask as
+ *             well (written by an extra pass; the prefill does not read it).
+ *  workspace  at least attn_block_sparse_prefill_workspace_bytes(shape, block_size) bytes.
+ */
+int attn_block_sparse_prefill(const attn_shape_t* shape, const void* q, attn_strides_t q_strides, const void* k,
+                              const void* v, attn_strides_t kv_strides, void* o, attn_strides_t o_strides,
+                              const int32_t* cache_off, int32_t window, const float* sink, float scale,
+                              int32_t block_size, double keep_mean, double keep_radius, double* tau_mean,
+                              double* tau_radius, uint8_t* block_mask_out, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
+/*
  * attn_block_list_from_mask -- compact a caller-made block mask
  * (device uint8 [rows, n_kb], nonzero = kept, rows = batch*n_heads*nQB) into the
  * block-list format attn_prefill reads (device int32 [rows, 1 + n_kb]).

@@ -11,6 +11,7 @@ The computation lives in hand-written HIP kernels behind the C ABI of
     attn_dsa_decode(q, k, v, qi, ki, wi, topk, cache_off=None, sink=None)
     attn_block_select(q, k, block_size=128, keep_mean=0.05, keep_radius=0.05, ...)
     attn_block_list_from_mask(mask)
+    attn_block_sparse_prefill(q, k, v, cache_off=None, window=0, sink=None, block_size=128, keep_mean=0.05, ...)
 
 PyTorch supplies device memory and the current stream only.  If the library has not
 been built, every call raises; there is no fallback path.
@@ -20,6 +21,8 @@ from .api import (  # noqa: F401
     attn_block_list_from_mask,
     attn_block_select,
     attn_block_select_workspace_bytes,
+    attn_block_sparse_prefill,
+    attn_block_sparse_prefill_workspace_bytes,
     attn_decode,
     attn_decode_noalloc,
     attn_decode_noalloc_max_scratch_bytes,

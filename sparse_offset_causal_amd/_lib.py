@@ -25,6 +25,8 @@ EXPORTS = (
     "attn_block_select_workspace_bytes",
     "attn_block_select",
     "attn_block_list_from_mask",
+    "attn_block_sparse_prefill_workspace_bytes",
+    "attn_block_sparse_prefill",
     "attn_last_error",
 )
 
@@ -91,6 +93,12 @@ def load() -> ctypes.CDLL:
     lib.attn_block_select.argtypes = [POINTER(AttnShape), P, AttnStrides, P, AttnStrides, P, c_int32, c_int32,
                                       c_double, c_double, P, P, P, P, P, c_size_t, P]
     lib.attn_block_select.restype = c_int
+    lib.attn_block_sparse_prefill_workspace_bytes.argtypes = [POINTER(AttnShape), c_int32]
+    lib.attn_block_sparse_prefill_workspace_bytes.restype = c_size_t
+    lib.attn_block_sparse_prefill.argtypes = [POINTER(AttnShape), P, AttnStrides, P, P, AttnStrides, P, AttnStrides,
+                                              P, c_int32, P, c_float, c_int32, c_double, c_double, P, P, P, P,
+                                              c_size_t, P]
+    lib.attn_block_sparse_prefill.restype = c_int
     lib.attn_block_list_from_mask.argtypes = [c_int64, c_int32, P, P, P]
     lib.attn_block_list_from_mask.restype = c_int
     lib.attn_last_error.argtypes = []

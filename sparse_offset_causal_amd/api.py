@@ -314,6 +314,48 @@ def attn_block_select(q, k, block_size=128, cache_off=None, window=0, keep_mean=
     return dict(mask=mask, list=lst, tau_mean=tau_mean, tau_radius=tau_radius)
 
 
+def attn_block_sparse_prefill_workspace_bytes(q, k, block_size=128) -> int:
+    return int(_lib.load().attn_block_sparse_prefill_workspace_bytes(_shape(q, k), int(block_size)))
+
+
+def attn_block_sparse_prefill(q, k, v, cache_off=None, window=0, sink=None, scale=None, block_size=128,
+                              keep_mean=0.05, keep_radius=0.05, tau_mean=None, tau_radius=None, want_mask=False,
+                              workspace=None, out=None):
+    """Block selection and block-sparse prefill in one call (see attn_block_sparse_prefill in
+    include/soc_attn.h).  Returns o, or (o, dict(mask, tau_mean, tau_radius)) with want_mask."""
+    _common(q, k, v, cache_off, sink)
+    o = _out(q, out)
+    B, Hq, Tq, d = q.shape
+    Hkv, Tk = k.shape[1], k.shape[2]
+    dev = q.device
+    if tau_mean is None:
+        if keep_mean < 0:
+            raise ValueError("keep_mean < 0 needs tau_mean")
+        tau_mean = torch.empty((B, Hq), dtype=torch.float64, device=dev)
+    if tau_radius is None:
+        if keep_radius < 0:
+            raise ValueError("keep_radius < 0 needs tau_radius")
+        tau_radius = torch.empty((B, Hkv), dtype=torch.float64, device=dev)
+    for name, t, shp in (("tau_mean", tau_mean, (B, Hq)), ("tau_radius", tau_radius, (B, Hkv))):
+        if t.dtype != torch.float64 or not t.is_cuda or tuple(t.shape) != shp or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float64 GPU tensor of shape {shp}")
+    mask = None
+    if want_mask:
+        mask = torch.empty((B, Hq, -(-Tq // block_size), -(-Tk // block_size)), dtype=torch.uint8, device=dev)
+    lib = _lib.load()
+    shape = _shape(q, k)
+    need = int(lib.attn_block_sparse_prefill_workspace_bytes(shape, int(block_size)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    rc = lib.attn_block_sparse_prefill(shape, q.data_ptr(), _strides(q), k.data_ptr(), v.data_ptr(), _strides(k),
+                                       o.data_ptr(), _strides(o), _ptr(cache_off), int(window), _ptr(sink),
+                                       float(scale or 0.0), int(block_size), float(keep_mean), float(keep_radius),
+                                       tau_mean.data_ptr(), tau_radius.data_ptr(), _ptr(mask), workspace.data_ptr(),
+                                       workspace.numel() * workspace.element_size(), _stream())
+    _check(rc)
+    return (o, dict(mask=mask, tau_mean=tau_mean, tau_radius=tau_radius)) if want_mask else o
+
+
 def attn_block_list_from_mask(mask):
     """Kept-block list (int32 [..., 1 + n_kb]) from a uint8 GPU block mask [..., n_kb]."""
     if mask.dtype != torch.uint8 or not mask.is_cuda or not mask.is_contiguous():

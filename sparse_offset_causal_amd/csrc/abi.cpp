@@ -665,11 +665,18 @@ size_t attn_block_select_workspace_bytes(const attn_shape_t* shape, int32_t bloc
   return select_layout(shape, block_size).total;
 }
 
-int attn_block_select(const attn_shape_t* shape, const void* q, attn_strides_t q_strides, const void* k,
-                      attn_strides_t k_strides, const int32_t* cache_off, int32_t window, int32_t block_size,
-                      double keep_mean, double keep_radius, double* tau_mean, double* tau_radius,
-                      uint8_t* block_mask, int32_t* block_list, void* workspace, size_t workspace_bytes,
-                      hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and workspace carving shared by attn_block_select and attn_block_sparse_prefill.
+// Returns ATTN_OK with *out filled, kNoWork for an empty call, or an error code.
+constexpr int kNoWork = 1;
+int select_setup(const attn_shape_t* shape, const void* q, attn_strides_t q_strides, const void* k,
+                 attn_strides_t k_strides, const int32_t* cache_off, int32_t window, int32_t block_size,
+                 double keep_mean, double keep_radius, double* tau_mean, double* tau_radius, uint8_t* block_mask,
+                 int32_t* block_list, void* workspace, size_t workspace_bytes, hipStream_t stream, bool need_mask,
+                 soc::SelectArgs* out) {
   int rc = check_shape(shape);
   if (rc) return rc;
   if (block_size < 1) return fail(ATTN_E_INVAL, "block_size must be >= 1");
@@ -678,13 +685,11 @@ int attn_block_select(const attn_shape_t* shape, const void* q, attn_strides_t q
     return fail(ATTN_E_UNSUPPORTED, "bf16 block selection supports head_dim 64 or 128");
   if (shape->dtype == ATTN_F32 && d != 16 && d != 32 && d != 64 && d != 128)
     return fail(ATTN_E_UNSUPPORTED, "f32 block selection supports head_dim 16, 32, 64 or 128");
-  if (shape->tq == 0 || shape->batch == 0) {
-    g_err.clear();
-    return ATTN_OK;
-  }
+  if (shape->tq == 0 || shape->batch == 0) return kNoWork;
   if (!q || !k) return fail(ATTN_E_INVAL, "q and k must be non-NULL device pointers");
-  if (!tau_mean || !tau_radius || !block_mask)
-    return fail(ATTN_E_INVAL, "tau_mean, tau_radius and block_mask must be non-NULL device pointers");
+  if (!tau_mean || !tau_radius || (need_mask && !block_mask))
+    return fail(ATTN_E_INVAL, need_mask ? "tau_mean, tau_radius and block_mask must be non-NULL device pointers"
+                                        : "tau_mean and tau_radius must be non-NULL device pointers");
   const size_t esz = elem_size(shape->dtype);
   if (!aligned16(q) || !aligned16(k)) return fail(ATTN_E_INVAL, "q and k must be 16-byte aligned");
   if (!strides_ok(q_strides, esz) || !strides_ok(k_strides, esz))
@@ -737,8 +742,72 @@ int attn_block_select(const attn_shape_t* shape, const void* q, attn_strides_t q
   a.ccount = reinterpret_cast<uint32_t*>(ws + L.ccount);
   a.pick = reinterpret_cast<int64_t*>(ws + L.pick);
   a.cand = reinterpret_cast<double*>(ws + L.cand);
+  *out = a;
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_block_select(const attn_shape_t* shape, const void* q, attn_strides_t q_strides, const void* k,
+                      attn_strides_t k_strides, const int32_t* cache_off, int32_t window, int32_t block_size,
+                      double keep_mean, double keep_radius, double* tau_mean, double* tau_radius,
+                      uint8_t* block_mask, int32_t* block_list, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  soc::SelectArgs a;
+  const int rc = select_setup(shape, q, q_strides, k, k_strides, cache_off, window, block_size, keep_mean, keep_radius,
+                              tau_mean, tau_radius, block_mask, block_list, workspace, workspace_bytes, stream, true, &a);
+  if (rc == kNoWork) {
+    g_err.clear();
+    return ATTN_OK;
+  }
+  if (rc) return rc;
   const hipError_t e = soc::launch_block_select(a, shape->dtype == ATTN_BF16, stream);
   return finish(e, stream, "attn_block_select launch");
+}
+
+size_t attn_block_sparse_prefill_workspace_bytes(const attn_shape_t* shape, int32_t block_size) {
+  return attn_block_select_workspace_bytes(shape, block_size);
+}
+
+int attn_block_sparse_prefill(const attn_shape_t* shape, const void* q, attn_strides_t q_strides, const void* k,
+                              const void* v, attn_strides_t kv_strides, void* o, attn_strides_t o_strides,
+                              const int32_t* cache_off, int32_t window, const float* sink, float scale,
+                              int32_t block_size, double keep_mean, double keep_radius, double* tau_mean,
+                              double* tau_radius, uint8_t* block_mask_out, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+  int rc = check_shape(shape);
+  if (rc) return rc;
+  if ((rc = check_attn_dtype(shape))) return rc;
+  if (shape->tq == 0 || shape->batch == 0) {
+    g_err.clear();
+    return ATTN_OK;
+  }
+  if ((rc = check_tensors(shape, q, q_strides, k, v, kv_strides, o, o_strides))) return rc;
+  if (shape->dtype == ATTN_BF16 && block_size != 128)
+    return fail(ATTN_E_UNSUPPORTED, "the bf16 block-sparse prefill needs block_size 128");
+  if (shape->dtype == ATTN_BF16 && (int64_t)shape->tk * kv_strides.t * 2 > (int64_t)0xffffffff)
+    return fail(ATTN_E_UNSUPPORTED, "one (sequence, KV head) cache slice spans more than 4 GiB (tk * token stride)");
+  const int64_t nqt = (shape->tq + 127) / 128;
+  if (nqt * shape->batch * shape->n_heads >= (int64_t)1 << 31) return fail(ATTN_E_INVAL, "problem too large for one grid");
+  soc::SelectArgs sa;
+  rc = select_setup(shape, q, q_strides, k, kv_strides, cache_off, window, block_size, keep_mean, keep_radius, tau_mean,
+                    tau_radius, block_mask_out, nullptr, workspace, workspace_bytes, stream, false, &sa);
+  if (rc) return rc;  // (kNoWork is excluded above)
+  hipError_t e = soc::launch_block_select(sa, shape->dtype == ATTN_BF16, stream);
+  if (e != hipSuccess) return hip_fail(e, "attn_block_sparse_prefill selection launch");
+  soc::AttnArgs a = make_args(shape, q, q_strides, k, v, kv_strides, o, o_strides, cache_off, window, sink, scale);
+  a.block_size = block_size;
+  a.n_qb = sa.nqb;
+  a.mask_stride = sa.nkb;
+  a.list_stride = 1 + sa.nkb;
+  a.sel_score = sa.score;
+  a.sel_rad2 = sa.rad2;
+  a.sel_tau_mean = tau_mean;
+  a.sel_tau_radius = tau_radius;
+  e = shape->dtype == ATTN_BF16 ? soc::launch_prefill_bf16(a, stream) : soc::launch_prefill_f32(a, stream);
+  return finish(e, stream, "attn_block_sparse_prefill prefill launch");
 }
 
 int attn_block_list_from_mask(int64_t rows, int32_t n_kb, const uint8_t* block_mask, int32_t* block_list,

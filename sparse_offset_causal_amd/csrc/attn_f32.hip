@@ -86,10 +86,16 @@ __global__ void __launch_bounds__(64) prefill_f32_kernel(AttnArgs a) {
       const int j0 = max(lo, kb * a.block_size), j1 = min(pos, kb * a.block_size + a.block_size - 1);
       if (j0 <= j1) st.run(q, kp, vp, a.kv_st, j0, j1, a.scale_log2);
     }
-  } else if (SPARSE) {  // block mask: the key blocks of the row's range that the mask marks
-    const uint8_t* mrow = a.block_mask + ((int64_t)(b * a.Hq + h) * a.n_qb + r / a.block_size) * a.mask_stride;
+  } else if (SPARSE) {  // block mask, or the block selection's scores: the key blocks of the row's range kept
+    const int64_t qrow = ((int64_t)(b * a.Hq + h) * a.n_qb + r / a.block_size) * a.mask_stride;
+    const uint8_t* mrow = a.block_mask ? a.block_mask + qrow : nullptr;
+    const double* srow = a.sel_score ? a.sel_score + qrow : nullptr;
+    const double* rrow = a.sel_score ? a.sel_rad2 + (int64_t)(b * a.Hkv + kvh) * a.mask_stride : nullptr;
+    const double t1 = a.sel_score ? a.sel_tau_mean[b * a.Hq + h] : 0.0;
+    const double t2 = a.sel_score ? a.sel_tau_radius[b * a.Hkv + kvh] : 0.0;
     for (int kb = lo / a.block_size; kb <= pos / a.block_size; ++kb) {
-      if (!mrow[kb]) continue;
+      const bool kept = mrow ? mrow[kb] != 0 : (srow[kb] > SOC_NEG_INF && (srow[kb] > t1 || rrow[kb] > t2));
+      if (!kept) continue;
       const int j0 = max(lo, kb * a.block_size), j1 = min(pos, kb * a.block_size + a.block_size - 1);
       st.run(q, kp, vp, a.kv_st, j0, j1, a.scale_log2);
     }
@@ -140,7 +146,7 @@ template <int D>
 hipError_t launch_prefill_f32_d(const AttnArgs& a, hipStream_t s) {
   const int64_t total = (int64_t)a.B * a.Hq * a.tq;
   const unsigned grid = (unsigned)((total + 63) / 64);
-  if (a.block_list || a.block_mask)
+  if (a.block_list || a.block_mask || a.sel_score)
     hipLaunchKernelGGL((prefill_f32_kernel<D, true>), dim3(grid), dim3(64), 0, s, a);
   else
     hipLaunchKernelGGL((prefill_f32_kernel<D, false>), dim3(grid), dim3(64), 0, s, a);

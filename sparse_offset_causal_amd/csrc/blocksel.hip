@@ -731,7 +731,8 @@ hipError_t launch_select_d(const SelectArgs& a, hipStream_t s) {
   }
   const unsigned gt = (mean_on ? a.B * a.Hq : 0) + (a.keep_radius >= 0.0 ? a.B * a.Hkv : 0);
   if (gt) hipLaunchKernelGGL(threshold_kernel, dim3(gt), dim3(1024), 0, s, a);
-  hipLaunchKernelGGL(mask_kernel, dim3((gq + NTHR / 64 - 1) / (NTHR / 64)), dim3(NTHR), 0, s, a);
+  if (a.mask)  // (the fused block-sparse prefill reads the scores and thresholds instead)
+    hipLaunchKernelGGL(mask_kernel, dim3((gq + NTHR / 64 - 1) / (NTHR / 64)), dim3(NTHR), 0, s, a);
   return hipGetLastError();
 }
 

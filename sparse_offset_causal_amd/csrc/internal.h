@@ -27,6 +27,12 @@ struct AttnArgs {
   const int32_t* block_list;  // device [B, Hq, n_qb, list_stride] or null
   const uint8_t* block_mask;  // device [B, Hq, n_qb, mask_stride] or null
   int32_t block_size, n_qb, list_stride, mask_stride;
+  // block-sparse prefill fused with block selection: the kept blocks are decided from the
+  // selection's scores [B, Hq, n_qb, mask_stride], radii [B, Hkv, mask_stride] and thresholds
+  const double* sel_score;
+  const double* sel_rad2;
+  const double* sel_tau_mean;    // [B, Hq]
+  const double* sel_tau_radius;  // [B, Hkv]
   // split-KV decode
   float* part;     // workspace: partial sums, [B*Hq*tq][nsplit][d] floats, then [..][nsplit][2]
   int32_t nsplit;  // splits per sequence (capacity)

@@ -11,7 +11,8 @@ import torch
 
 import synth
 from oracle import attend, block_list_from_mask, select_blocks
-from sparse_offset_causal_amd import attn_block_list_from_mask, attn_block_select, attn_prefill
+from sparse_offset_causal_amd import (attn_block_list_from_mask, attn_block_select, attn_block_sparse_prefill,
+                                      attn_prefill)
 from tests.gpu_helpers import BF16_TOL, announce, dev, host64, max_abs, require_gpu
 
 pytestmark = pytest.mark.gpu
@@ -132,3 +133,52 @@ def test_block_sparse_prefill_on_selected_blocks():
     o = attn_prefill(dev(w.q), dev(w.k), dev(w.v), block_list=sel["list"], block_size=128)
     ref = attend(w.q, w.k, w.v, block_mask=ref_sel["mask"], block_size=128)
     assert max_abs(o, ref) <= BF16_TOL
+
+
+# ---------------------------------------------------------------- fused selection + prefill
+@pytest.mark.parametrize("case", [
+    # B, Hq, Hkv, Tq, Tk, offsets, window, sink, keeps
+    (1, 8, 2, 2048, 2048, None, 0, False, (0.1, 0.125)),       # planted-outlier prompt, one shot
+    (3, 8, 2, 300, 1500, [1200, 37, 640], 0, True, (0.1, 0.1)),  # query-chunked: chunks at cache offsets
+    (2, 16, 4, 384, 1400, [1000, 500], 700, True, (0.2, 0.05)),  # chunks with a window
+])
+def test_fused_block_sparse_prefill(case):
+    """attn_block_sparse_prefill, which decides each key block inside the prefill from the
+    selection's scores and thresholds, equals the two-call route (attn_block_select, then
+    attn_prefill over its mask) bit for bit, writes the same mask when asked, and matches the
+    oracle: its selection at the same offsets, then attention over that mask."""
+    B, Hq, Hkv, Tq, Tk, offs, W, with_sink, (km, kr) = case
+    announce(f"fused block-sparse prefill {case}")
+    if offs is None:
+        w = synth.block_sparse_prefill(T=Tq, BS=128, Hq=Hq, Hkv=Hkv, d=128, frac=0.125)
+        w.cache_off = None
+    else:
+        w = synth.attention_inputs(B, Hq, Hkv, Tq, Tk, 128, torch.bfloat16, seed=Tq + Tk, with_sink=with_sink,
+                                   window=W, cache_off=offs)
+    q, k, v = dev(w.q), dev(w.k), dev(w.v)
+    off = None if w.cache_off is None else dev(w.cache_off)
+    sink = dev(w.sink) if with_sink else None
+    o, sel = attn_block_sparse_prefill(q, k, v, cache_off=off, window=W, sink=sink, keep_mean=km, keep_radius=kr,
+                                       want_mask=True)
+    o_plain = attn_block_sparse_prefill(q, k, v, cache_off=off, window=W, sink=sink, keep_mean=km, keep_radius=kr)
+    two = attn_block_select(q, k, block_size=128, cache_off=off, window=W, keep_mean=km, keep_radius=kr)
+    assert torch.equal(sel["mask"], two["mask"])
+    o_two = attn_prefill(q, k, v, cache_off=off, window=W, sink=sink, block_mask=two["mask"], block_size=128)
+    assert torch.equal(o, o_two) and torch.equal(o_plain, o_two)
+    ref_sel = select_blocks(w.q, w.k, 128, cache_off=None if offs is None else offs, window=W, keep_mean=km,
+                            keep_radius=kr)
+    assert min_gap(ref_sel) > REL_EPS
+    assert np.array_equal(sel["mask"].cpu().numpy(), ref_sel["mask"])
+    ref = attend(w.q, w.k, w.v, cache_off=w.cache_off, window=W, sink=w.sink if with_sink else None,
+                 block_mask=ref_sel["mask"], block_size=128)
+    assert max_abs(o, ref) <= BF16_TOL
+
+
+def test_fused_block_sparse_prefill_f32():
+    w = synth.attention_inputs(2, 4, 2, 70, 150, 32, torch.float32, seed=41, with_sink=True, cache_off=[80, 33])
+    o, sel = attn_block_sparse_prefill(dev(w.q), dev(w.k), dev(w.v), cache_off=dev(w.cache_off), sink=dev(w.sink),
+                                       block_size=16, keep_mean=0.2, keep_radius=0.1, want_mask=True)
+    ref_sel = select_blocks(w.q, w.k, 16, cache_off=[80, 33], keep_mean=0.2, keep_radius=0.1)
+    assert np.array_equal(sel["mask"].cpu().numpy(), ref_sel["mask"])
+    ref = attend(w.q, w.k, w.v, cache_off=w.cache_off, sink=w.sink, block_mask=ref_sel["mask"], block_size=16)
+    assert max_abs(o, ref) <= 1e-5
