@@ -5,7 +5,9 @@ import ctypes
 import os
 from ctypes import POINTER, c_double, c_float, c_int, c_int32, c_int64, c_size_t, c_uint8, c_void_p
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsoc_attn.so")
+# SOC_ATTN_LIB names another build of the same library (the sanitized host build the ABI
+# tests run under); by default the in-tree build is loaded.
+LIB_PATH = os.environ.get("SOC_ATTN_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsoc_attn.so")
 
 ATTN_BF16, ATTN_F32 = 0, 1
 ATTN_OK, ATTN_E_INVAL, ATTN_E_UNSUPPORTED, ATTN_E_WORKSPACE, ATTN_E_HIP = 0, -1, -2, -3, -4

@@ -64,5 +64,43 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     return LIB
 
 
+SANITIZED_LIB = os.path.join(BUILD, "libsoc_attn_asan.so")
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """The same library with its host code (the C ABI layer) built under AddressSanitizer and
+    UndefinedBehaviorSanitizer (device code unchanged: the sanitizers apply to the host pass
+    only), for running the argument-checking tests on the CPU.  Load it with the ASan runtime
+    preloaded (sanitizer_runtime()).  Written to _build/, never loaded by the package itself."""
+    os.makedirs(BUILD, exist_ok=True)
+    objs = [os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in SOURCES if s.endswith(".hip")]
+    if not all(os.path.exists(o) for o in objs):
+        build(verbose)
+    abi_obj = os.path.join(BUILD, "abi_asan.o")
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-Xarch_host",
+           "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+    cmd = [hipcc(), *FLAGS, *san, "-x", "hip", "-c", os.path.join(CSRC, "abi.cpp"), "-o", abi_obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on abi.cpp (sanitized):\n{r.stdout}\n{r.stderr}")
+    cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=gfx950", "-Xarch_host", "-fsanitize=address", "-Xarch_host",
+           "-fsanitize=undefined", "-shared-libsan", abi_obj, *objs, "-o", SANITIZED_LIB]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed (sanitized):\n{r.stdout}\n{r.stderr}")
+    return SANITIZED_LIB
+
+
+def sanitizer_runtime() -> str:
+    """Path of the ASan runtime (which carries the UBSan handlers) to preload into Python."""
+    r = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    return r.stdout.strip()
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "sanitized" in sys.argv[1:]:
+        print(build_sanitized(verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))
