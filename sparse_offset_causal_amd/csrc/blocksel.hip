@@ -37,6 +37,8 @@ namespace soc {
 namespace {
 
 constexpr int NTHR = 256;
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+typedef double f64x2 __attribute__((ext_vector_type(2)));
 
 // 8 consecutive elements of a row, loaded raw and widened to double on use.
 template <typename T>
@@ -86,6 +88,36 @@ __device__ __forceinline__ bool admissible(const SelectArgs& a, int off, int tkb
 // together).
 constexpr int RB = 8;
 
+// Cross-lane moves of a double, as two 32-bit halves.
+__device__ __forceinline__ uint32_t lo32(double x) { return (uint32_t)__builtin_bit_cast(uint64_t, x); }
+__device__ __forceinline__ uint32_t hi32(double x) { return (uint32_t)(__builtin_bit_cast(uint64_t, x) >> 32); }
+__device__ __forceinline__ double from32(uint32_t lo, uint32_t hi) {
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+// x(l) + x(l ^ 32) and x(l) + x(l ^ 16) with gfx950's lane-swap VALU instructions: both lanes of
+// a pair get the same sum (the lower lane's value first).
+__device__ __forceinline__ double sum_xor32(double x) {
+  const auto l = __builtin_amdgcn_permlane32_swap(lo32(x), lo32(x), false, false);
+  const auto h = __builtin_amdgcn_permlane32_swap(hi32(x), hi32(x), false, false);
+  return from32(l[0], h[0]) + from32(l[1], h[1]);
+}
+__device__ __forceinline__ double sum_xor16(double x) {
+  const auto l = __builtin_amdgcn_permlane16_swap(lo32(x), lo32(x), false, false);
+  const auto h = __builtin_amdgcn_permlane16_swap(hi32(x), hi32(x), false, false);
+  return from32(l[0], h[0]) + from32(l[1], h[1]);
+}
+// A DPP lane permutation of a double (CTRL: quad_perm, row_ror or row_half_mirror code).
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const uint32_t l = (uint32_t)__builtin_amdgcn_mov_dpp((int)lo32(x), CTRL, 0xf, 0xf, false);
+  const uint32_t h = (uint32_t)__builtin_amdgcn_mov_dpp((int)hi32(x), CTRL, 0xf, 0xf, false);
+  return from32(l, h);
+}
+constexpr int DPP_XOR1 = 0xB1;         // quad_perm [1, 0, 3, 2]
+constexpr int DPP_XOR2 = 0x4E;         // quad_perm [2, 3, 0, 1]
+constexpr int DPP_HALF_MIRROR = 0x141;  // lane i <-> 7 - i within each 8 lanes
+constexpr int DPP_ROR8 = 0x128;         // lane i <-> i ^ 8 within each 16 lanes
+
 // Block mean of rows [r0, r1) of a [rows, D] matrix (row stride st), written to out_lds[D].
 // Thread layout: C = D/8 threads per row (8 columns each), NTHR/C row groups; a thread adds
 // its rows in ascending order, then the row groups are added in ascending order.  When the
@@ -112,13 +144,32 @@ __device__ bool block_mean(const T* base, int64_t st, int r0, int r1, double* re
       }
     }
   }
+  if (C == 16) {
+    // The wave's 4 row groups (lanes c, c + 16, c + 32, c + 48) are summed with lane swaps;
+    // lane (j, c) then writes columns 8c + 2j, 8c + 2j + 1, so each wave stores one
+    // contiguous, conflict-free 1 KB row of partial column sums; the 4 waves are added in
+    // order.
 #pragma unroll
-  for (int e = 0; e < 8; ++e) red[rg * D + 8 * c + e] = acc[e];
-  __syncthreads();
-  if (threadIdx.x < D) {
-    double sum = 0.0;
-    for (int g = 0; g < RG; ++g) sum += red[g * D + threadIdx.x];
-    out_lds[threadIdx.x] = sum / (double)(r1 - r0);
+    for (int e = 0; e < 8; ++e) acc[e] = sum_xor16(sum_xor32(acc[e]));
+    const int lane = threadIdx.x & 63, j = lane >> 4;
+    f64x2 w2;
+    w2[0] = j == 0 ? acc[0] : j == 1 ? acc[2] : j == 2 ? acc[4] : acc[6];
+    w2[1] = j == 0 ? acc[1] : j == 1 ? acc[3] : j == 2 ? acc[5] : acc[7];
+    *(f64x2*)(red + (threadIdx.x >> 6) * D + 8 * c + 2 * j) = w2;
+    __syncthreads();
+    if (threadIdx.x < D) {
+      const double sum = ((red[threadIdx.x] + red[D + threadIdx.x]) + red[2 * D + threadIdx.x]) + red[3 * D + threadIdx.x];
+      out_lds[threadIdx.x] = sum / (double)(r1 - r0);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[rg * D + 8 * c + e] = acc[e];
+    __syncthreads();
+    if (threadIdx.x < D) {
+      double sum = 0.0;
+      for (int g = 0; g < RG; ++g) sum += red[g * D + threadIdx.x];
+      out_lds[threadIdx.x] = sum / (double)(r1 - r0);
+    }
   }
   __syncthreads();
   return r1 - r0 <= RB * RG;
@@ -188,22 +239,57 @@ __device__ __forceinline__ void kstats_block(const SelectArgs& a, int id, double
         if (r < r1) rows[u].load(base + (int64_t)r * a.k_st + 8 * c);
       }
     }
+    double part[RB];
 #pragma unroll
     for (int u = 0; u < RB; ++u) {
       const int r = rb + u * RG;
-      double part = 0.0;
+      part[u] = 0.0;
       if (r < r1) {
         double x[8];
         rows[u].widen(x);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const double dlt = x[e] - cv[e];
-          part = fma(dlt, dlt, part);
+          part[u] = fma(dlt, dlt, part[u]);
         }
       }
+    }
+    if (C == 16) {
+      // Reduce-scatter of the 8 rows' partial sums over the 16 lanes of the row group in four
+      // DPP exchanges: each round a lane keeps half of its rows (by one bit of its index) and
+      // adds the partner's values for them; afterwards lanes 2m and 2m + 1 both hold row
+      // slot m's full sum (m = bits 3..1 of the lane index).
+      const int i = threadIdx.x & 15;
+      double k4[4], k2[2], k1;
 #pragma unroll
-      for (int m = 1; m < C; m <<= 1) part += __shfl_xor(part, m, 64);
-      if (r < r1) best = fmax(best, part);
+      for (int t = 0; t < 4; ++t) {
+        const bool up = i & 8;
+        const double keep = up ? part[4 + t] : part[t], send = up ? part[t] : part[4 + t];
+        k4[t] = keep + dpp_f64<DPP_ROR8>(send);
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const bool up = i & 4;
+        const double keep = up ? k4[2 + t] : k4[t], send = up ? k4[t] : k4[2 + t];
+        k2[t] = keep + dpp_f64<DPP_HALF_MIRROR>(send);
+      }
+      {
+        const bool up = i & 2;
+        const double keep = up ? k2[1] : k2[0], send = up ? k2[0] : k2[1];
+        k1 = keep + dpp_f64<DPP_XOR2>(send);
+      }
+      // (addition commutes exactly, so both lanes of the pair get the same sum; the exchange
+      // runs in every lane: a DPP move under a partial exec mask would read disabled lanes)
+      const double total = k1 + dpp_f64<DPP_XOR1>(k1);
+      if (rb + ((i >> 1) & 7) * RG < r1) best = fmax(best, total);
+    } else {
+#pragma unroll
+      for (int u = 0; u < RB; ++u) {
+        double pu = part[u];
+#pragma unroll
+        for (int m = 1; m < C; m <<= 1) pu += __shfl_xor(pu, m, 64);
+        if (rb + u * RG < r1) best = fmax(best, pu);
+      }
     }
   }
 #pragma unroll
@@ -267,8 +353,6 @@ struct BucketMap {
 };
 
 constexpr int ST = kScoreTile;
-typedef double f64x4 __attribute__((ext_vector_type(4)));
-typedef double f64x2 __attribute__((ext_vector_type(2)));
 
 // s1 = <qmean, c> on the fp64 MFMA (v_mfma_f64_16x16x4f64: A[i][k] in lane i + 16k, B[k][j]
 // in lane j + 16k, D[i][j] in lane j + 16 (i % 4), element i / 4), one 64 x 64 tile of
