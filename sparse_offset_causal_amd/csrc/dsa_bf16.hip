@@ -13,13 +13,16 @@
 //                       rows, so that every wave ends at about the same time: scores^T =
 //                       Ki Qi^T with v_mfma_f32_16x16x32_bf16 (16 tokens x 16 indexer heads per
 //                       MFMA), ReLU and the head weights in fp32, the sum over heads in a fixed
-//                       order (DPP within each 16-lane row)
+//                       order (DPP within each 16-lane row); with each score, a bound on its
+//                       fp32 rounding error (one more MFMA per 32 dims)
 //   dsa_topk_kernel     one 1024-thread workgroup per (sequence, query token): radix select of
-//                       the k-th largest score on order-preserving 32-bit keys (digits of 12,
-//                       12 and 8 bits; the first histogram is built while the keys are staged
-//                       in LDS), then an index-ordered compaction (ties at the threshold:
-//                       lowest indices) into an ascending list, one contiguous token segment
-//                       per wave
+//                       the k-th largest fp32 score on order-preserving 32-bit keys (digits of
+//                       12, 12 and 8 bits; the first histogram is built while the keys are
+//                       staged in LDS); the tokens within twice the largest error bound of
+//                       that threshold are scored again in fp64 (fp64 MFMA) and ranked there,
+//                       so the kept set is exactly the top k of the fp64 scores (ties: lower
+//                       index); then an index-ordered compaction into an ascending list, one
+//                       contiguous token segment per wave
 //   dsa_split_kernel    split-KV decode over the kept list: one wave per (sequence, KV head,
 //                       query token, split of the list); K rows are gathered by index straight
 //                       into registers and V rows by index into LDS (buffer loads with the LDS
