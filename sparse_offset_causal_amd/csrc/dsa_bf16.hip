@@ -251,41 +251,6 @@ __device__ __forceinline__ unsigned wave_suffix_sum(unsigned x) {
   return x;
 }
 
-// One wave finds the bin holding descending rank `rank` of an NB-bin histogram and the rank
-// within that bin: lane l first sums bins [G l, G l + G), then the chosen group's G bins are
-// searched one per lane (G = 64) or in turn (G = 4).
-template <int NB>
-__device__ void locate_digit(const unsigned* hist, unsigned rank, unsigned* digit, unsigned* rank_in) {
-  constexpr int G = NB / 64;
-  const int lane = threadIdx.x & 63;
-  unsigned c = 0;
-#pragma unroll
-  for (int j = 0; j < G; ++j) c += hist[G * lane + j];
-  const unsigned s = wave_suffix_sum(c);
-  const unsigned ab = s - c;
-  const unsigned long long own = __ballot(ab <= rank && rank < s);
-  const int L = own ? __ffsll(own) - 1 : 0;
-  unsigned r = rank - (unsigned)__builtin_amdgcn_readlane((int)ab, L);
-  if constexpr (G == 64) {
-    const unsigned h = hist[G * L + lane];
-    const unsigned s2 = wave_suffix_sum(h);
-    const unsigned ab2 = s2 - h;
-    const unsigned long long own2 = __ballot(ab2 <= r && r < s2);
-    const int j = own2 ? __ffsll(own2) - 1 : 0;
-    *digit = G * L + j;
-    *rank_in = r - (unsigned)__builtin_amdgcn_readlane((int)ab2, j);
-  } else {
-    int e = G - 1;
-    for (; e > 0; --e) {
-      const unsigned h = hist[G * L + e];
-      if (r < h) break;
-      r -= h;
-    }
-    *digit = G * L + e;
-    *rank_in = r;
-  }
-}
-
 constexpr int TOPK_LDS = 32768;  // scores of up to this many visible tokens are staged in LDS
 constexpr int TOPK_BINS = 4096;  // digits of 12, 12 and 8 bits (32-bit keys); 12 x 4, 8 x 2 (64-bit)
 
@@ -329,7 +294,7 @@ constexpr int BAND_LDS = 1024;  // band sizes decided in LDS; larger bands by fp
 
 __global__ void __launch_bounds__(1024) dsa_topk_kernel(DsaArgs A) {
   const AttnArgs& a = A.at;
-  __shared__ __attribute__((aligned(8))) unsigned hist[TOPK_BINS];
+  __shared__ __attribute__((aligned(16))) unsigned hist[TOPK_BINS];
   __shared__ unsigned su[2];
   __shared__ unsigned wcnt[2][16];
   __shared__ unsigned red[16];
@@ -363,35 +328,56 @@ __global__ void __launch_bounds__(1024) dsa_topk_kernel(DsaArgs A) {
   if (tid == 0) nband_s = 0;
   __syncthreads();
   float emax = 0.f;
-  for (int i0 = tid; i0 < n_vis; i0 += 4 * 1024) {
-    uint32_t kv[4];
-    float ev[4];
+  for (int i0 = tid; i0 < n_vis; i0 += 16 * 1024) {
+    // 16 scores and 16 bounds per thread in flight (one round for 16384 tokens)
+    float sv[16], ev[16];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 16; ++u) {
       const int i = i0 + 1024 * u;
-      kv[u] = i < n_vis ? f32_order_key(sc[i]) : 0u;
+      sv[u] = i < n_vis ? sc[i] : 0.f;
       ev[u] = i < n_vis ? eb[i] : 0.f;
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 16; ++u) {
       const int i = i0 + 1024 * u;
       emax = fmaxf(emax, ev[u]);
       if (i < n_vis) {
-        if (staged) keys[i] = kv[u];
-        atomicAdd(&hist[kv[u] >> 20], 1u);
+        const uint32_t kv = f32_order_key(sv[u]);
+        if (staged) keys[i] = kv;
+        atomicAdd(&hist[kv >> 20], 1u);
       }
     }
   }
   __syncthreads();
   unsigned rank = (unsigned)(K - 1);
+  // The bin holding descending rank `rank` of an NB-bin histogram, and the rank inside it:
+  // thread t owns bins 4t .. 4t+3 (one conflict-free 16-byte read), each wave sums its 256
+  // bins, the wave holding the rank is found from the 16 wave totals, then its lane, then the
+  // bin (higher bins = higher keys = lower descending ranks).
+  __shared__ unsigned wtot[16];
   auto pick = [&](auto nb_tag) __attribute__((always_inline)) -> unsigned {  // digit; updates rank
     constexpr int NB = decltype(nb_tag)::value;
-    if (wave == 0) {
-      unsigned dg, r;
-      locate_digit<NB>(hist, rank, &dg, &r);
-      if (lane == 0) {
-        su[0] = dg;
-        su[1] = r;
+    u32x4 h4 = {0u, 0u, 0u, 0u};
+    if (4 * tid < NB) h4 = *(const u32x4*)(hist + 4 * tid);
+    const unsigned c = h4[0] + h4[1] + h4[2] + h4[3];
+    const unsigned sfx = wave_suffix_sum(c);  // this lane's and the higher lanes' bins
+    if (lane == 0) wtot[wave] = sfx;
+    __syncthreads();
+    unsigned above = 0;  // count in the waves above this one
+    for (int w = 15; w > wave; --w) above += wtot[w];
+    const unsigned wt = wtot[wave];
+    if (above <= rank && rank < above + wt) {  // (wave-uniform) the rank lies in this wave
+      const unsigned r = rank - above;
+      const unsigned ab = sfx - c;
+      if (ab <= r && r < sfx) {  // exactly one lane
+        unsigned rr = r - ab;
+        int e = 3;
+        for (; e > 0; --e) {
+          if (rr < h4[e]) break;
+          rr -= h4[e];
+        }
+        su[0] = 4 * tid + e;
+        su[1] = rr;
       }
     }
     __syncthreads();
@@ -403,9 +389,13 @@ __global__ void __launch_bounds__(1024) dsa_topk_kernel(DsaArgs A) {
   auto count32 = [&](int shift, unsigned dmask, int nb) __attribute__((always_inline)) {
     for (int i = tid; i < nb; i += 1024) hist[i] = 0;
     __syncthreads();
-    for (int i = tid; i < n_vis; i += 1024) {
-      const uint32_t key = key_at(i);
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1u);
+    for (int i0 = tid; i0 < n_vis; i0 += 8 * 1024) {  // 8 key reads in flight
+      uint32_t kk[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) kk[u] = i0 + 1024 * u < n_vis ? key_at(i0 + 1024 * u) : ~prefix;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (i0 + 1024 * u < n_vis && (kk[u] & pmask) == prefix) atomicAdd(&hist[(kk[u] >> shift) & dmask], 1u);
     }
     __syncthreads();
   };
@@ -425,30 +415,63 @@ __global__ void __launch_bounds__(1024) dsa_topk_kernel(DsaArgs A) {
   // that score.  The kept set is then the top K of the fp64 scores, equal scores to the lower
   // token index.
   const double bw = 2.0 * kScoreErrBound * (double)block_max_f(emax, red);
+  // The two comparisons as key comparisons: s32 > x iff s32 > (the largest float <= x), and
+  // s32 < y iff s32 < (the smallest float >= y); consecutive keys are consecutive floats.
+  uint32_t key_hi, key_lo;
+  {
+    const double x = tau32 + bw, y = tau32 - bw;
+    key_hi = f32_order_key((float)x);
+    if ((double)f32_of_key(key_hi) > x) key_hi -= 1u;
+    key_lo = f32_order_key((float)y);
+    if ((double)f32_of_key(key_lo) < y) key_lo += 1u;
+  }
   auto certain = [&](uint32_t key) __attribute__((always_inline)) -> int {  // 2 kept, 0 dropped, 1 band
-    const double s32 = (double)f32_of_key(key);
-    return s32 > tau32 + bw ? 2 : s32 < tau32 - bw ? 0 : 1;
+    return key > key_hi ? 2 : key < key_lo ? 0 : 1;
   };
+  // Wave w owns the contiguous token segment [w * seg, (w + 1) * seg): the classification
+  // counts each segment's certain keeps, the decision adds each segment's band keeps, and the
+  // compaction writes every segment's kept tokens at the offset those counts give.
+  const int seg = ((n_vis + 16 * 64 - 1) / (16 * 64)) * 64;
+  const int w0 = wave * seg, w1 = min(w0 + seg, n_vis);
+  __shared__ unsigned wkeep[16];
   // the band in small rows lives in LDS, in the histogram's space (free from here on)
   uint64_t* bkey = reinterpret_cast<uint64_t*>(hist);
   int32_t* bidx = reinterpret_cast<int32_t*>(hist + 2 * BAND_LDS);
   static_assert(3 * BAND_LDS <= TOPK_BINS, "band arrays fit in the histogram's LDS");
-  unsigned n_in = 0;
-  for (int i0 = 0; i0 < n_vis; i0 += 1024) {
-    const int i = i0 + tid;
-    const int c = i < n_vis ? certain(key_at(i)) : 0;
-    n_in += c == 2;
-    const unsigned long long bb = __ballot(c == 1);
-    unsigned base = 0;
-    if (lane == 0 && bb) base = atomicAdd(&nband_s, (unsigned)__popcll(bb));
-    base = __builtin_amdgcn_readfirstlane(base);
-    if (c == 1) {
-      const unsigned e = base + (unsigned)__popcll(bb & ((1ull << lane) - 1ull));
-      band[e] = i;
-      if (e < BAND_LDS) bidx[e] = i;
+  unsigned gt_w = 0;  // this wave's certain keeps
+  for (int c0 = w0; c0 < w0 + seg; c0 += 4 * 64) {  // (seg is a multiple of 64) 4 key reads in flight
+    int cls[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = c0 + 64 * u + lane;
+      cls[u] = c0 + 64 * u < w0 + seg && i < w1 ? certain(key_at(i)) : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = c0 + 64 * u + lane;
+      const int c = cls[u];
+      gt_w += (unsigned)__popcll(__ballot(c == 2));
+      const unsigned long long bb = __ballot(c == 1);
+      if (bb) {  // (wave-uniform) band tokens in this chunk: rare
+        unsigned base = 0;
+        if (lane == 0) base = atomicAdd(&nband_s, (unsigned)__popcll(bb));
+        base = __builtin_amdgcn_readfirstlane(base);
+        if (c == 1) {
+          const unsigned e = base + (unsigned)__popcll(bb & ((1ull << lane) - 1ull));
+          band[e] = i;
+          if (e < BAND_LDS) bidx[e] = i;
+        }
+      }
     }
   }
-  n_in = block_sum_u(n_in, red);  // (its barriers also publish nband_s and the band lists)
+  if (lane == 0) {
+    wcnt[0][wave] = gt_w;
+    wkeep[wave] = 0u;
+  }
+  __syncthreads();  // (also publishes nband_s and the band lists)
+  unsigned n_in = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) n_in += wcnt[0][w];
   const int n_band = (int)nband_s;
   const bool in_lds = n_band <= BAND_LDS;
   const int R = K - (int)n_in;  // band tokens to keep (>= 1)
@@ -465,52 +488,66 @@ __global__ void __launch_bounds__(1024) dsa_topk_kernel(DsaArgs A) {
     const int slot = lane & 15, G = lane >> 4;
     const bf16_t* kbase = (const bf16_t*)A.ki + b * A.ki_sb;
     const int ngroups = (n_band + 15) / 16;
-    for (int grp = wave; grp < ngroups; grp += 16) {
-      const int e = min(grp * 16 + slot, n_band - 1);  // slots past the band repeat its last token
-      const int tok = in_lds ? bidx[e] : band[e];
-      const u32x4* kp = (const u32x4*)(kbase + (int64_t)tok * A.ki_st + 32 * G);
-      double sacc[4] = {0.0, 0.0, 0.0, 0.0};  // tokens 4v + G
-      for (int ht = 0; ht < Hi; ht += 16) {
-        const int head = ht + slot;
+    const int ntiles = (Hi + 15) / 16;  // head tiles of 16 (at most 16)
+    const int gpr = 16 / ntiles;        // groups per round: one (group, head tile) item per wave
+    // the items' partial sums over their 16 heads: 16 tokens each, in the histogram's last
+    // quarter (free: the band keys and indices use the first three)
+    double* part = reinterpret_cast<double*>(hist + 3 * BAND_LDS);
+    static_assert(16 * 16 * sizeof(double) <= BAND_LDS * sizeof(unsigned), "partials fit");
+    for (int g0 = 0; g0 < ngroups; g0 += gpr) {
+      const int grp = g0 + wave / ntiles, tile = wave % ntiles;
+      if (wave < gpr * ntiles && grp < ngroups) {
+        const int e = min(grp * 16 + slot, n_band - 1);  // slots past the band repeat its last token
+        const int tok = in_lds ? bidx[e] : band[e];
+        const u32x4* kp = (const u32x4*)(kbase + (int64_t)tok * A.ki_st + 32 * G);
+        const int head = tile * 16 + slot;
         const bool hok = head < Hi;
         const u32x4* qp = (const u32x4*)((const bf16_t*)A.qi + b * A.qi_sb + (hok ? head : 0) * A.qi_sh + t * A.qi_st + 32 * G);
+        u32x4 kc[4], qc[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          kc[c] = kp[c];
+          qc[c] = hok ? qp[c] : u32x4{0u, 0u, 0u, 0u};
+        }
         const double wj = hok ? (double)A.wi[((int64_t)b * Hi + head) * a.tq + t] : 0.0;
         f64x4 acc = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll 1
-        for (int c = 0; c < 4; ++c) {  // 8 steps per 16 bytes of key and query (L1 hits after the first tile)
-          const u32x4 kc = kp[c];
-          const u32x4 qc = hok ? qp[c] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {  // 8 steps per 16 bytes of key and query
 #pragma unroll
           for (int m = 0; m < 8; ++m) {
-            const uint32_t kw = kc[m >> 1], qw2 = qc[m >> 1];
+            const uint32_t kw = kc[c][m >> 1], qw2 = qc[c][m >> 1];
             const double av = (double)((m & 1) ? bf16_hi(kw) : bf16_lo(kw));
             const double bv = (double)((m & 1) ? bf16_hi(qw2) : bf16_lo(qw2));
             acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc, 0, 0, 0);
           }
+          __builtin_amdgcn_sched_barrier(0);  // converts one chunk at a time (registers)
         }
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           double term = wj * (acc[v] > 0.0 ? acc[v] : 0.0);
 #pragma unroll
           for (int o = 1; o < 16; o <<= 1) term += __shfl_xor(term, o, 64);  // the tile's 16 heads
-          sacc[v] += term;
+          if (slot == 0) part[wave * 16 + 4 * v + G] = term;  // token 4v + G of the group
         }
       }
-      if (slot == 0) {
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int ei = grp * 16 + 4 * v + G;
-          if (ei < n_band) {
-            if (in_lds)
-              bkey[ei] = f64_key(sacc[v]);
-            else
-              s64[band[ei]] = sacc[v];
-          }
+      __syncthreads();
+      // each group's score: its tiles' partials added in head order (a fixed order: equal key
+      // rows get equal scores)
+      if (tid < gpr * 16) {
+        const int gi = tid >> 4, sl = tid & 15;
+        const int ei = (g0 + gi) * 16 + sl;
+        if (g0 + gi < ngroups && ei < n_band) {
+          double sc64 = 0.0;
+          for (int ti = 0; ti < ntiles; ++ti) sc64 += part[(gi * ntiles + ti) * 16 + sl];
+          if (in_lds)
+            bkey[ei] = f64_key(sc64);
+          else
+            s64[band[ei]] = sc64;
         }
       }
+      __syncthreads();
     }
   }
-  __syncthreads();
 
   uint64_t tau64 = 0;
   unsigned need_eq = 0;
@@ -537,6 +574,7 @@ __global__ void __launch_bounds__(1024) dsa_topk_kernel(DsaArgs A) {
         keys[itok] = dec;
       else
         const_cast<float*>(sc)[itok] = f32_of_key(dec);
+      if (dec == KEY_POS_INF) atomicAdd(&wkeep[itok / seg], 1u);
     }
   } else {
     // fp64 radix select over the band: descending rank R - 1 (digits of 12 x 4, 8 x 2)
@@ -578,8 +616,23 @@ __global__ void __launch_bounds__(1024) dsa_topk_kernel(DsaArgs A) {
     const uint64_t k64 = f64_key(s64[i]);
     return k64 > tau64 ? 2 : k64 == tau64 ? 1 : 0;
   };
-  const int seg = ((n_vis + 16 * 64 - 1) / (16 * 64)) * 64;
-  const int w0 = wave * seg, w1 = min(w0 + seg, n_vis);
+  const unsigned long long lt_mask = (1ull << lane) - 1ull;
+  if (in_lds) {
+    // every key is now decided (band keys were set to +-inf): each segment's keeps are its
+    // certain keeps plus its band keeps, so one pass writes them at their offsets
+    unsigned out = 0;
+    for (int w = 0; w < wave; ++w) out += wcnt[0][w] + wkeep[w];
+    for (int c0 = w0; c0 < w0 + seg; c0 += 64) {
+      const int i = c0 + lane;
+      const bool keep = i < w1 && key_at(i) > key_hi;
+      const unsigned long long bk = __ballot(keep);
+      const unsigned pos = out + (unsigned)__popcll(bk & lt_mask);
+      if (keep && pos < (unsigned)K) lst[pos] = i;
+      out += (unsigned)__popcll(bk);
+    }
+    if (tid == 0) A.count[b * a.tq + t] = K;
+    return;
+  }
   unsigned gt_c = 0, eq_c = 0;
   for (int c0 = w0; c0 < w0 + seg; c0 += 64) {
     const int i = c0 + lane;
@@ -599,7 +652,6 @@ __global__ void __launch_bounds__(1024) dsa_topk_kernel(DsaArgs A) {
     out += g + (e < left ? e : left);
     eq_seen += e;
   }
-  const unsigned long long lt_mask = (1ull << lane) - 1ull;
   for (int c0 = w0; c0 < w0 + seg; c0 += 64) {
     const int i = c0 + lane;
     const int c = i < w1 ? cls_at(i) : 0;
