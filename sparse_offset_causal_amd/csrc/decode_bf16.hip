@@ -29,6 +29,9 @@
 //     step waits until at most 16 loads are outstanding: if any of block n's 8 K or 8 V
 //     loads were still pending, the 16 loads of the same kind issued after it (blocks n+1
 //     and n+2) would be pending too.  One younger block stays in flight.
+//     The wait orders memory accesses only, so the K registers pass through an empty asm
+//     after it: otherwise the compiler may schedule the QK MFMAs above it, guarded by its own
+//     counts, which assume one in-order stream of loads.
 //   * a stage's transposed reads have completed before the DMA that refills it is issued:
 //     each step ends with lgkmcnt(0).
 // Each stage is a separate LDS variable, so the compiler can tell which stage a pending DMA
@@ -341,6 +344,12 @@ decode_split_bf16_d128(AttnArgs a) {
     constexpr int ST = decltype(stage_tag)::value;
     issue(min(n + NST - 1, nblk - 1), std::integral_constant<int, (ST + NST - 1) % NST>{});
     wait_blocks<NST - 1>();  // block n's K registers and V stage have landed
+    // The wait orders memory accesses only: an MFMA reading the K registers could still be
+    // scheduled above it, guarded just by the compiler's own count, which takes all loads as
+    // one ordered stream.  Passing the registers through an empty asm after the wait ties
+    // their use to it.
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) asm volatile("" : "+v"(kreg[ST][ks]));
     const bf16_t* vt = vstage(stage_tag);
     const int js = kbeg + n * KB;
     if (RING && own_slot && slot >= js && slot < js + KB) {  // uniform: the ring slot being overwritten

@@ -777,6 +777,12 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) ds
     // each retire in issue order but not in order with each other, so the wait allows only
     // the 8 * (NST - 1) loads of one kind that were issued after block n's.
     vm_wait<8 * (NST - 1)>();
+    // The wait orders memory accesses only: an MFMA reading the K registers could still be
+    // scheduled above it, guarded just by the compiler's own count, which takes all loads as
+    // one ordered stream.  Passing the registers through an empty asm after the wait ties
+    // their use to it.
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) asm volatile("" : "+v"(kreg[ST][ks]));
     const bf16_t* vt = vstage(stage_tag);
     const int js = ks0 + n * KB;  // list position of the block's first entry
 
