@@ -656,7 +656,7 @@ int attn_dsa_decode(const attn_shape_t* shape, const void* q, attn_strides_t q_s
   A.band = reinterpret_cast<int32_t*>(ws + L.band);
   A.list = kept_list ? kept_list : reinterpret_cast<int32_t*>(ws + L.list);
   A.count = kept_count ? kept_count : reinterpret_cast<int32_t*>(ws + L.count);
-  A.idx_waves = 12 * device_cus();  // three single-wave workgroups per SIMD (148 VGPRs each)
+  A.idx_waves = device_cus();  // one 12-wave indexer workgroup per CU
   return finish(soc::launch_dsa_decode(A, stream), stream, "attn_dsa_decode launch");
 }
 

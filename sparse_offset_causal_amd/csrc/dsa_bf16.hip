@@ -8,11 +8,13 @@
 // visible); equal scores go to the lower token index.  Every head of the query token attends
 // over the same kept set.
 //
-//   dsa_indexer_kernel  a fixed grid of single-wave workgroups (three per SIMD), each scoring
-//                       an equal share of all 16-token blocks of all (sequence, query token)
-//                       rows, so that every wave ends at about the same time: scores^T =
-//                       Ki Qi^T with v_mfma_f32_16x16x32_bf16 (16 tokens x 16 indexer heads per
-//                       MFMA), ReLU and the head weights in fp32, the sum over heads in a fixed
+//   dsa_indexer_kernel  one 12-wave workgroup per CU, each scoring an equal share of all
+//                       16-token blocks of all (sequence, query token) rows, in phases of up
+//                       to 4 rows whose queries sit in LDS; the waves take blocks from a
+//                       counter in LDS (4 at a time), keep 4 blocks of keys in flight each,
+//                       and leave scores in LDS until the phase ends: scores^T = Ki Qi^T with
+//                       v_mfma_f32_16x16x32_bf16 (16 tokens x 16 indexer heads per MFMA),
+//                       ReLU and the head weights in fp32, the sum over heads in a fixed
 //                       order (DPP within each 16-lane row); with each score, a bound on its
 //                       fp32 rounding error (one more MFMA per 32 dims)
 //   dsa_topk_kernel     one 1024-thread workgroup per (sequence, query token): radix select of
@@ -99,27 +101,74 @@ __device__ __forceinline__ int wave_incl_prefix_i(int x) {
   return x;
 }
 
-__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) dsa_indexer_kernel(DsaArgs A) {
+// Waits go through the s_waitcnt builtin: the compiler treats it as touching all memory (no
+// LDS access moves across it) and knows what it waited for, so it adds no drain of its own.
+// gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N <= 63, "vmcnt counts at most 63 loads");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void lds_wait() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
+
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+
+constexpr int IDX_WAVES = 12;  // waves of the indexer workgroup (one workgroup per CU)
+constexpr int IDX_NB = 5;      // key blocks per wave in registers: IDX_NB - 1 in flight while one is scored
+constexpr int IDX_RMAX = 4;    // rows whose queries a phase stages in LDS
+constexpr int IDX_GRAB = 4;    // blocks a wave takes from the phase's counter at a time
+constexpr int IDX_PB = 600;    // blocks of a phase (their scores and bounds wait in LDS)
+
+// One row segment of a phase: row b * tq + t, its blocks j0 .. j0 + len - 1, staged from
+// block u0 of the phase.
+struct IdxSeg {
+  int b, t, nvis, j0, len, u0;
+};
+// x_s of four values for an index s (by value: selecting whole segments, or through
+// references, turns into indexed private memory)
+__device__ __forceinline__ int sel4(int s, int x0, int x1, int x2, int x3) {
+  return s >= 2 ? (s == 3 ? x3 : x2) : (s == 1 ? x1 : x0);
+}
+
+// One workgroup per CU scores a contiguous share of the 16-token blocks of all rows (row
+// r = b * tq + t has ceil(n_vis / 16) blocks; rows in order).  The share is cut into phases
+// of at most IDX_RMAX row segments and IDX_PB blocks.  In a phase the waves take blocks one
+// at a time from a counter in LDS, so the CU's waves finish together however unevenly the
+// memory system serves them (a static split leaves the last waves streaming alone); every
+// score and bound goes to LDS, and the phase's outputs are written once all its blocks are
+// scored, so no store is in flight beside the key loads and the compiler counts those loads
+// exactly.
+__global__ void __launch_bounds__(64 * IDX_WAVES) __attribute__((amdgpu_waves_per_eu(3))) dsa_indexer_kernel(DsaArgs A) {
   const AttnArgs& a = A.at;
-  __shared__ __attribute__((aligned(16))) bf16_t ulds[DI];
-  const int lane = threadIdx.x, G = lane >> 4, i16 = lane & 15;
+  // query tiles: head h's 16-byte piece c at piece c ^ (h & 15) of its 256-byte row (the
+  // B-operand reads of 16 heads then hit 16 different bank groups)
+  __shared__ __attribute__((aligned(16))) bf16_t qlds[IDX_RMAX][kDsaMaxIndexHeads * DI];
+  __shared__ __attribute__((aligned(16))) bf16_t ulds[IDX_RMAX][DI];
+  __shared__ float wlds[IDX_RMAX][kDsaMaxIndexHeads];
+  __shared__ __attribute__((aligned(16))) float sst[2][IDX_PB * 16];  // scores, bounds
+  __shared__ unsigned ucnt[2];                                         // block counters, by phase parity
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int G = lane >> 4, i16 = lane & 15;
   const int rows = a.B * a.tq;
-  // Row r = b * tq + t has nb(r) = ceil(n_vis / 16) blocks of 16 tokens; the blocks of all
-  // rows, in row order, are split evenly over the waves of the grid.
-  auto row_blocks = [&](int r) __attribute__((always_inline)) -> int {
+  auto row_nvis = [&](int r) __attribute__((always_inline)) -> int {  // visible tokens of row r (0 past the end)
     if (r >= rows) return 0;
     const int b = r / a.tq, t = r - b * a.tq;
-    return (min(a.tk, seq_off(a, b) + t + 1) + 15) >> 4;
+    return min(a.tk, seq_off(a, b) + t + 1);
   };
-  int total = 0;
-  for (int r0 = 0; r0 < rows; r0 += 64) total += wave_sum_i(row_blocks(r0 + lane));
+  // Lane l holds n_vis of row rwin + l.  The first window also gives the total when there
+  // are at most 64 rows, so the offsets are read once.
+  int rwin = 0, nvw = row_nvis(lane);
+  int total = wave_sum_i((nvw + 15) >> 4);
+  for (int r0 = 64; r0 < rows; r0 += 64) total += wave_sum_i((row_nvis(r0 + lane) + 15) >> 4);
   total = __builtin_amdgcn_readfirstlane(total);
   const int W = gridDim.x, wid = blockIdx.x;
-  const int lo = (int)((int64_t)total * wid / W), hi = (int)((int64_t)total * (wid + 1) / W);
-  if (lo >= hi) return;
+  const int lo = __builtin_amdgcn_readfirstlane((int)((int64_t)total * wid / W));
+  const int hi = __builtin_amdgcn_readfirstlane((int)((int64_t)total * (wid + 1) / W));
+  if (lo >= hi) return;  // (uniform over the workgroup)
   int row = 0, rstart = 0;  // the row holding block lo and the global index of its first block
   for (int r0 = 0, base = 0; r0 < rows; r0 += 64) {
-    const int nb = row_blocks(r0 + lane);
+    if (r0 != rwin) rwin = r0, nvw = row_nvis(r0 + lane);
+    const int nb = (nvw + 15) >> 4;
     const int incl = base + wave_incl_prefix_i(nb);
     const unsigned long long own = __ballot(nb > 0 && incl - nb <= lo && lo < incl);
     if (own) {
@@ -132,110 +181,204 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3))) ds
   }
   row = __builtin_amdgcn_readfirstlane(row);
   rstart = __builtin_amdgcn_readfirstlane(rstart);
+  rwin = __builtin_amdgcn_readfirstlane(rwin);
+  if (tid < 2) ucnt[tid] = 0;
+  __syncthreads();
 
   const int nhb = A.Hi / 16;
+  const int qper = A.Hi * (DI / 8);  // 16-byte query pieces per row
   const uint32_t row_bytes = (uint32_t)A.ki_st * 2u;
-  const u32x4 z = {0u, 0u, 0u, 0u};
-  for (int g = lo; g < hi;) {
-    const int b = __builtin_amdgcn_readfirstlane(row / a.tq);
-    const int t = __builtin_amdgcn_readfirstlane(row - b * a.tq);
-    const int n_vis = __builtin_amdgcn_readfirstlane(min(a.tk, seq_off(a, b) + t + 1));
-    const int nb_row = (n_vis + 15) >> 4;
-    bf16x8 qb[4][4];
-    float w[4];
-#pragma unroll
-    for (int hb = 0; hb < 4; ++hb) {
-      const int head = 16 * hb + i16;
-      const bool ok = hb < nhb;
-      const bf16_t* qp = (const bf16_t*)A.qi + b * A.qi_sb + head * A.qi_sh + t * A.qi_st;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) qb[hb][ks] = ok ? *(const bf16x8*)(qp + 32 * ks + 8 * G) : as_bf16x8(z);
-      w[hb] = ok ? A.wi[((int64_t)b * A.Hi + head) * a.tq + t] : 0.f;
-    }
-    // Error-bound weights u[d] = sum_j |w_j| |qi_j[d]| of this query token, rounded up to bf16,
-    // kept in LDS (ulds) and read as a B operand broadcast to all 16 columns: the MFMA of |k|
-    // against it gives E = u . |k|, which bounds the fp32 rounding of the token's score.
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      bf16x8 uv;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float p = 0.f;
-#pragma unroll
-        for (int hb = 0; hb < 4; ++hb) p = fmaf(fabsf(w[hb]), fabsf((float)qb[hb][ks][e]), p);
-        uv[e] = bf16_round_up(row16_sum(p) * kBoundSumSlack);
+  for (int g = lo, phase = 0; g < hi; ++phase) {
+    // The phase's row segments (unused ones empty, with u0 past every block).
+    auto next_seg = [&](int used) __attribute__((always_inline)) -> IdxSeg {
+      IdxSeg sg{0, 0, 1, 0, 0, used};
+      if (g < hi && used < IDX_PB) {  // uniform
+        if (row >= rwin + 64) rwin = row, nvw = row_nvis(row + lane);
+        const int nvis = __builtin_amdgcn_readlane(nvw, row - rwin);
+        const int nb = (nvis + 15) >> 4, j0 = g - rstart;
+        const int len = min(min(nb - j0, hi - g), IDX_PB - used);
+        sg.b = __builtin_amdgcn_readfirstlane(row / a.tq);
+        sg.t = __builtin_amdgcn_readfirstlane(row - sg.b * a.tq);
+        sg.nvis = nvis, sg.j0 = __builtin_amdgcn_readfirstlane(j0), sg.len = __builtin_amdgcn_readfirstlane(len);
+        g += len;
+        if (j0 + len == nb) rstart += nb, ++row;
       }
-      if (i16 == 0) *(bf16x8*)(ulds + 32 * ks + 8 * G) = uv;
-    }
-    const bf16_t* kp = (const bf16_t*)A.ki + b * A.ki_sb;
-    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kp, (short)0, (int)(n_vis * row_bytes), 0x00020000);
-    float* out = A.scores + ((int64_t)b * a.tq + t) * a.tk;
-    const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc((void*)out, (short)0, (int)(n_vis * 4), 0x00020000);
-    float* eout = A.ebound + ((int64_t)b * a.tq + t) * a.tk;
-    const __amdgpu_buffer_rsrc_t ers = __builtin_amdgcn_make_buffer_rsrc((void*)eout, (short)0, (int)(n_vis * 4), 0x00020000);
-    const int j0 = g - rstart, j1 = min(nb_row, hi - rstart);  // this wave's blocks of the row
-    auto load = [&](bf16x8* af, int j) __attribute__((always_inline)) {
-      const int tok0 = 16 * j;
+      return sg;
+    };
+    static_assert(IDX_RMAX == 4, "four segments below");
+    const IdxSeg S0 = next_seg(0);
+    const IdxSeg S1 = next_seg(S0.u0 + S0.len);
+    const IdxSeg S2 = next_seg(S1.u0 + S1.len);
+    const IdxSeg S3 = next_seg(S2.u0 + S2.len);
+    const int nunits = S3.u0 + S3.len;
+    const int ns = 1 + (S1.len > 0) + (S2.len > 0) + (S3.len > 0);
+    auto seg_of = [&](int u) __attribute__((always_inline)) -> int { return (u >= S1.u0) + (u >= S2.u0) + (u >= S3.u0); };
+
+    // Block u of the phase, clamped to the last one (the loads past a wave's last block).
+    auto load = [&](bf16x8* af, int u) __attribute__((always_inline)) {
+      u = min(u, nunits - 1);
+      const int s = seg_of(u);
+      const int tok0 = 16 * (u + sel4(s, S0.j0 - S0.u0, S1.j0 - S1.u0, S2.j0 - S2.u0, S3.j0 - S3.u0));
+      const bf16_t* kp = (const bf16_t*)A.ki + sel4(s, S0.b, S1.b, S2.b, S3.b) * A.ki_sb;
+      const int nvis = sel4(s, S0.nvis, S1.nvis, S2.nvis, S3.nvis);
+      const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kp, (short)0, (int)(nvis * row_bytes), 0x00020000);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
         af[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
                                                 krs, (uint32_t)(tok0 + i16) * row_bytes + (uint32_t)(64 * ks + 16 * G), 0, 0));
     };
-    auto score = [&](const bf16x8* af, int j) __attribute__((always_inline)) {
-      const int tok0 = 16 * j;
+    auto score = [&](const bf16x8* af, int u) __attribute__((always_inline)) {
+      const int s = seg_of(u);
+      const bf16_t* qs = qlds[0] + s * (kDsaMaxIndexHeads * DI);
       float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int hb = 0; hb < 4; ++hb) {
         if (hb >= nhb) break;  // uniform
+        const bf16_t* qrow = qs + (16 * hb + i16) * DI;  // head 16 hb + i16
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) acc = mfma16k32(af[ks], qb[hb][ks], acc);
+        for (int ks = 0; ks < 4; ++ks) acc = mfma16k32(af[ks], *(const bf16x8*)(qrow + 8 * ((4 * ks + G) ^ i16)), acc);
+        const float wv = wlds[0][s * kDsaMaxIndexHeads + 16 * hb + i16];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) part[v] = fmaf(w[hb], fmaxf(acc[v], 0.f), part[v]);
+        for (int v = 0; v < 4; ++v) part[v] = fmaf(wv, fmaxf(acc[v], 0.f), part[v]);
       }
-      // lane (G, i16): tokens 4G + v, indexer head i16 of each block; sum over the 16 heads.
-      // Lane i16 == 0 of each group stores through a buffer whose range ends at the row's
-      // last visible token; the other lanes' stores fall outside the range and are dropped
-      // (no branch, so the compiler can keep counting the key loads still in flight).
+      // lane (G, i16): tokens 4G + v, indexer head i16 of each tile; sum over the 16 heads
 #pragma unroll
       for (int v = 0; v < 4; ++v) part[v] = row16_sum(part[v]);
-      // E = u . |k| for tokens 4G + v (every column; lanes i16 == 0 store it).  The empty asm
-      // makes the LDS address opaque, so the reads stay here instead of holding u in registers.
-      const bf16_t* ua = ulds + 8 * G;
+      // E = u . |k| for tokens 4G + v (every column; lanes i16 == 0 keep it).  The empty asm
+      // makes the LDS address opaque, so the reads stay here instead of holding u in registers;
+      // the cast back to the LDS address space keeps them LDS reads (a generic pointer would
+      // make them flat loads, which the compiler must also count against the key loads).
+      const bf16_t* ua = ulds[0] + s * DI + 8 * G;
       asm volatile("" : "+v"(ua));
+      const lds_bf16x8* ul = (const lds_bf16x8*)ua;
       f32x4 eacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        eacc = mfma16k32(as_bf16x8(as_u32x4(af[ks]) & 0x7fff7fffu), *(const bf16x8*)(ua + 32 * ks), eacc);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const uint32_t at = i16 == 0 ? (uint32_t)(tok0 + 4 * G + v) * 4u : 0x80000000u;
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, part[v]), ors, at, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, eacc[v]), ers, at, 0, 0);
+      for (int ks = 0; ks < 4; ++ks) eacc = mfma16k32(as_bf16x8(as_u32x4(af[ks]) & 0x7fff7fffu), ul[4 * ks], eacc);
+      if (i16 == 0) {
+        *(f32x4*)&sst[0][u * 16 + 4 * G] = f32x4{part[0], part[1], part[2], part[3]};
+        *(f32x4*)&sst[1][u * 16 + 4 * G] = f32x4{eacc[0], eacc[1], eacc[2], eacc[3]};
       }
     };
-    // the keys of blocks j + 1 and j + 2 are in flight while block j is scored (three
-    // rotating buffers; with one block ahead the waves held too few bytes in flight to
-    // cover the memory latency)
-    // Every load is issued unconditionally (past the segment's last block it reloads that
-    // block), so the number of loads in flight is the same on every path.
-    bf16x8 fa[4], fb[4], fc[4];
-    const int jl = j1 - 1;
-    load(fa, min(j0, jl));
-    load(fb, min(j0 + 1, jl));
-    for (int j = j0; j < j1; j += 3) {
-      load(fc, min(j + 2, jl));
-      score(fa, j);
-      if (j + 1 >= j1) break;
-      load(fa, min(j + 3, jl));
-      score(fb, j + 1);
-      if (j + 2 >= j1) break;
-      load(fb, min(j + 4, jl));
-      score(fc, j + 2);
+    // A wave takes IDX_GRAB consecutive blocks per counter access (one access per block cost
+    // 4 us over the workgroup's waves); the next batch is requested when the current one
+    // starts and read when it is needed, so the access's latency stays out of the way.
+    unsigned* cnt = &ucnt[phase & 1];
+    unsigned nxt = 0;  // (lane 0) first block of the wave's next batch
+    int cur = 0, left = 0;
+    auto fetch = [&]() __attribute__((always_inline)) {
+      if (lane == 0) nxt = __hip_atomic_fetch_add(cnt, (unsigned)IDX_GRAB, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    };
+    auto grab = [&]() __attribute__((always_inline)) -> int {  // the wave's next block of the phase
+      if (left == 0) {  // uniform
+        cur = __builtin_amdgcn_readfirstlane((int)nxt), left = IDX_GRAB;
+        fetch();
+      }
+      --left;
+      return cur++;
+    };
+
+    // The phase's queries go straight into LDS (1 KB = 4 heads per wave instruction), with the
+    // head weights into registers.  Whatever is still counted first retires (after the first
+    // phase: the previous phase's stores and its last, unused key loads).
+    vm_wait<0>();
+    // Each block id is taken one step before its load is issued.  The first ids are taken
+    // before the query copies start: the compiler cannot tell the counter from their
+    // destination and would make every later counter access wait for them.
+    fetch();
+    int uid[IDX_NB];
+#pragma unroll
+    for (int k = 0; k < IDX_NB - 1; ++k) uid[k] = grab();
+    int pend = grab();
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    for (int n = wave; n < ns * (A.Hi / 4); n += IDX_WAVES) {  // 4 heads of one row per instruction
+      const int s = n / (A.Hi / 4), h = 4 * (n - s * (A.Hi / 4)) + (lane >> 4);
+      const bf16_t* qb = (const bf16_t*)A.qi + sel4(s, S0.b, S1.b, S2.b, S3.b) * A.qi_sb + sel4(s, S0.t, S1.t, S2.t, S3.t) * A.qi_st;
+      const __amdgpu_buffer_rsrc_t qrs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)qb, (short)0, (int)(A.Hi * A.qi_sh * 2), 0x00020000);
+      const uint32_t voff = (uint32_t)(h * A.qi_sh + 8 * ((lane & 15) ^ (h & 15))) * 2u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (lds_void_ptr)(qlds[0] + s * (kDsaMaxIndexHeads * DI) + (h - (lane >> 4)) * DI), 16, voff, 0, 0, 0);
     }
-    g = rstart + j1;
-    rstart += nb_row;
-    ++row;
+    float wv = 0.f;
+    if (tid < ns * A.Hi) {
+      const int s = tid / A.Hi, j = tid - s * A.Hi;
+      wv = A.wi[((int64_t)sel4(s, S0.b, S1.b, S2.b, S3.b) * A.Hi + j) * a.tq + sel4(s, S0.t, S1.t, S2.t, S3.t)];
+    }
+    // The first key blocks go out once every wave's query copies are in, so the copies do not
+    // queue behind them, and they are in flight while the error-bound weights are formed.
+    vm_wait<0>();
+    if (tid < ns * A.Hi) wlds[0][(tid / A.Hi) * kDsaMaxIndexHeads + tid % A.Hi] = wv;
+    __syncthreads();
+    bf16x8 fbuf[IDX_NB][4];
+#pragma unroll
+    for (int k = 0; k < IDX_NB - 1; ++k) load(fbuf[k], uid[k]);
+    // u[d] = sum_j |w_j| |qi_j[d]| (fp32, rounded up to bf16 with a slack covering the sum's
+    // rounding in any order) is read as a B operand broadcast to all 16 columns, so the MFMA
+    // of |k| against it gives E = u . |k|, which bounds the fp32 rounding of the score.  Item
+    // (s, quarter of the heads, pair of dims) sums its 16 heads; the quarters are added in
+    // order after a barrier (the score stage is free until the blocks are scored).
+    {
+      float* part = sst[0];  // [s][quarter][d]
+      const int hq = A.Hi / 4;
+      for (int i = tid; i < ns * 4 * (DI / 2); i += 64 * IDX_WAVES) {
+        const int s = i / (4 * (DI / 2)), r = i % (4 * (DI / 2)), q4 = r / (DI / 2), d = 2 * (r % (DI / 2));
+        float p0 = 0.f, p1 = 0.f;
+#pragma unroll 8
+        for (int j = q4 * hq; j < (q4 + 1) * hq; ++j) {
+          const float w = fabsf(wlds[s][j]);
+          const uint32_t qq = *(const uint32_t*)&qlds[s][j * DI + 8 * ((d >> 3) ^ (j & 15)) + (d & 7)];
+          p0 = fmaf(w, fabsf(__builtin_bit_cast(float, qq << 16)), p0);
+          p1 = fmaf(w, fabsf(__builtin_bit_cast(float, qq & 0xffff0000u)), p1);
+        }
+        part[(s * 4 + q4) * DI + d] = p0;
+        part[(s * 4 + q4) * DI + d + 1] = p1;
+      }
+      __syncthreads();
+      for (int i = tid; i < ns * DI; i += 64 * IDX_WAVES) {
+        const int s = i / DI, d = i % DI;
+        const float p = ((part[(s * 4) * DI + d] + part[(s * 4 + 1) * DI + d]) + part[(s * 4 + 2) * DI + d]) + part[(s * 4 + 3) * DI + d];
+        ulds[s][d] = bf16_round_up(p * kBoundSumSlack);
+      }
+    }
+    __syncthreads();
+
+    // IDX_NB rotating register buffers: a block is scored while the wave's next IDX_NB - 1
+    // are in flight.  A wave's ids rise in the order of its buffers, so once a buffer holds an
+    // id past the phase, so do all after it.  Every step issues its load (past the phase it
+    // reloads the phase's last block) and only the scoring is skipped, and the loop is left
+    // only at the top of a round: the same loads are in flight on every path, so the compiler
+    // counts them exactly (an exit in mid-round would be merged into the loop's latch).
+    for (;;) {
+      if (uid[0] >= nunits) break;  // uniform
+#pragma unroll
+      for (int u = 0; u < IDX_NB; ++u) {
+        const int nx = (u + IDX_NB - 1) % IDX_NB;
+        const int cur = uid[u];
+        uid[nx] = pend;
+        pend = grab();
+        load(fbuf[nx], uid[nx]);
+        if (cur < nunits) score(fbuf[u], cur);  // uniform
+      }
+    }
+    __syncthreads();  // every block of the phase is scored
+    // The phase's scores and bounds go out, two tokens per thread and round, through buffers
+    // whose range ends at the row's last visible token.
+    auto flush = [&](const IdxSeg sg) __attribute__((always_inline)) {
+      const int64_t r = (int64_t)sg.b * a.tq + sg.t;
+      const uint32_t nbytes = (uint32_t)sg.nvis * 4u;
+      const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc((void*)(A.scores + r * a.tk), (short)0, (int)nbytes, 0x00020000);
+      const __amdgpu_buffer_rsrc_t ers = __builtin_amdgcn_make_buffer_rsrc((void*)(A.ebound + r * a.tk), (short)0, (int)nbytes, 0x00020000);
+      for (int i = 2 * tid; i < 16 * sg.len; i += 2 * 64 * IDX_WAVES) {
+        const uint32_t at = (uint32_t)(16 * sg.j0 + i) * 4u;
+        const int e = 16 * sg.u0 + i;
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sst[0][e]), ors, at, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sst[0][e + 1]), ors, at + 4u, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sst[1][e]), ers, at, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sst[1][e + 1]), ers, at + 4u, 0, 0);
+      }
+    };
+    flush(S0), flush(S1), flush(S2), flush(S3);
+    if (tid == 0) ucnt[phase & 1] = 0;  // used again two phases on, after several barriers
   }
 }
 
@@ -669,16 +812,6 @@ __global__ void __launch_bounds__(1024) dsa_topk_kernel(DsaArgs A) {
 // ---------------------------------------------------------------------------------------
 __device__ __forceinline__ int v_off(int row, int chunk) { return row * D + ((chunk ^ ((row & 3) << 2)) << 3); }
 
-// Waits go through the s_waitcnt builtin: the compiler treats it as touching all memory (no
-// LDS access moves across it) and knows what it waited for, so it adds no drain of its own.
-// gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8.
-template <int N>
-__device__ __forceinline__ void vm_wait() {
-  static_assert(N >= 0 && N <= 63, "vmcnt counts at most 63 loads");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-__device__ __forceinline__ void lds_wait() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
-
 static_assert(16 * (NST - 1) <= 63, "vmcnt holds at most 63 outstanding loads");
 
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) dsa_split_kernel(DsaArgs A) {
@@ -870,7 +1003,7 @@ hipError_t launch_dsa_decode(const DsaArgs& A, hipStream_t s) {
   const AttnArgs& a = A.at;
   const int64_t rows = (int64_t)a.B * a.tq;
   if (rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(dsa_indexer_kernel, dim3((unsigned)A.idx_waves), dim3(64), 0, s, A);
+  hipLaunchKernelGGL(dsa_indexer_kernel, dim3((unsigned)A.idx_waves), dim3(64 * IDX_WAVES), 0, s, A);
   hipLaunchKernelGGL(dsa_topk_kernel, dim3((unsigned)rows), dim3(1024), 0, s, A);
   hipLaunchKernelGGL(dsa_split_kernel, dim3((unsigned)(rows * a.Hkv * a.nsplit)), dim3(64), 0, s, A);
   // every split has a partial: the merge reads all nsplit of them (no offsets, tk = nsplit * split)

@@ -152,7 +152,7 @@ struct DsaArgs {
   int32_t* band;        // workspace [B, tq, tk]  those tokens' indices (any order)
   int32_t* list;        // [B, tq, topk] kept token indices, ascending
   int32_t* count;       // [B, tq]
-  int32_t idx_waves;    // waves of the indexer grid (each scores an equal share of all blocks)
+  int32_t idx_waves;    // workgroups of the indexer grid (one per CU; each scores an equal share of all blocks)
 };
 hipError_t launch_dsa_decode(const DsaArgs& a, hipStream_t s);
 

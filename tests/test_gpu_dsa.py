@@ -96,6 +96,23 @@ def test_dsa_decode_full_size_B64_topk2048():
     check(x, 2048, batches=sorted({0, 13, 37, 63, int(np.argmin(L)), int(np.argmax(L))}))
 
 
+def test_dsa_decode_many_short_rows_per_workgroup():
+    """2048 short rows (64 sequences x 32 query tokens, 100-300 cached tokens): each indexer
+    workgroup's share of the blocks spans about eight rows, more than one phase stages, so
+    shares are cut into several phases, and row windows past the first 64 rows are read."""
+    announce("dsa decode 64 x 32 short rows")
+    x = synth.dsa_inputs(B=64, Hq=8, Hkv=8, tq=32, lo=100, hi=300, Hi=16, seed=31)
+    check(x, 64, batches=[0, 21, 63])
+
+
+def test_dsa_decode_long_rows_multi_phase():
+    """8 sequences of 300k-320k cached tokens: each indexer workgroup's share exceeds the
+    blocks one phase holds, so a row's blocks are split over phases (and over workgroups)."""
+    announce("dsa decode 8 x ~310k tokens")
+    x = synth.dsa_inputs(B=8, Hq=8, Hkv=1, lo=300000, hi=320000, Hi=16, seed=32)
+    check(x, 256, batches=[0, 5])
+
+
 def test_dsa_decode_rejects_bad_index_heads():
     x = synth.dsa_inputs(B=1, Hq=8, Hkv=2, lengths=[10], Hi=8, seed=1)
     with pytest.raises(AttnError, match="index_heads"):
