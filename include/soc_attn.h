@@ -327,18 +327,17 @@ size_t attn_block_sparse_prefill_workspace_bytes(const attn_shape_t* shape, int3
  * attn_block_sparse_prefill -- block selection and block-sparse prefill in one call (patty.io
  * RBS-Attention review: the mean-centroid and max-radius sieves chosen per prompt and head, and
  * the regular block-sparse execution they feed, section on how regular sparsity persuades the
- * GPU).  Computes exactly attn_block_select's mask followed by attn_prefill over it, but the
- * prefill decides each key block itself from the selection's fp64 scores, squared radii and
- * thresholds held in the workspace (kept iff admissible and (s1 > tau_mean or rad2 >
- * tau_radius)): no mask or kept list is written or read between the two.  With a cache offset
- * this is the query-chunked selection of a chunked prefill: query block qb covers rows
+ * GPU).  Computes exactly attn_block_select's mask followed by attn_prefill over it: the
+ * selection's last pass writes the byte mask (into the workspace, or block_mask_out) and the
+ * prefill walks each row's marked key blocks straight from it; no kept list is built.  With a
+ * cache offset this is the query-chunked selection of a chunked prefill: query block qb covers rows
  * [qb*bs, (qb+1)*bs) of the tq-row chunk, key blocks are absolute.
  *  q, k, v, o, cache_off, window, sink, scale: as attn_prefill (bf16: head_dim 128).
  *  block_size, keep_mean, keep_radius, tau_mean, tau_radius: as attn_block_select (bf16:
  *             block_size 128); the thresholds are written (or read, with a negative keep
  *             fraction) as there.
- *  block_mask_out  NULL, or device uint8 [batch, n_heads, nQB, nKB] to receive the mask as
- *             well (written by an extra pass; the prefill does not read it).
+ *  block_mask_out  NULL, or device uint8 [batch, n_heads, nQB, nKB] to receive the mask (the
+ *             prefill then reads it from there instead of the workspace).
  *  workspace  at least attn_block_sparse_prefill_workspace_bytes(shape, block_size) bytes.
  */
 int attn_block_sparse_prefill(const attn_shape_t* shape, const void* q, attn_strides_t q_strides, const void* k,

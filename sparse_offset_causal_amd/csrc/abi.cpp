@@ -136,7 +136,7 @@ size_t round_up(size_t x, size_t m) { return (x + m - 1) / m * m; }
 
 struct SelectLayout {
   int nqb, nkb;
-  size_t qmean, cT, rad2, score, norm2, nmax, hpart, tflag, ccount, pick, cand, total;  // byte offsets, total
+  size_t qmean, cT, rad2, score, norm2, nmax, hpart, tflag, ccount, pick, cand, cpos, wmask, total;  // byte offsets
 };
 
 SelectLayout select_layout(const attn_shape_t* s, int bs) {
@@ -158,18 +158,21 @@ SelectLayout select_layout(const attn_shape_t* s, int bs) {
   off = round_up(off + d8 * (bh * L.nqb + (size_t)s->batch * s->n_kv * L.nkb), 256);
   L.nmax = off;
   off = round_up(off + d8 * (bh + (size_t)s->batch * s->n_kv), 256);
-  const size_t tiles = (size_t)((L.nqb + soc::kScoreTile - 1) / soc::kScoreTile) *
-                       ((L.nkb + soc::kScoreTile - 1) / soc::kScoreTile);
+  const size_t items = (size_t)soc::sel_items_per_head(L.nqb, L.nkb);
   L.hpart = off;
-  off = round_up(off + sizeof(uint16_t) * bh * tiles * soc::kSelBuckets, 256);
+  off = round_up(off + sizeof(uint16_t) * bh * items * soc::kSelBuckets, 256);
   L.tflag = off;
-  off = round_up(off + sizeof(uint32_t) * bh * tiles, 256);
+  off = round_up(off + sizeof(uint32_t) * bh * items, 256);
   L.ccount = off;
-  off = round_up(off + sizeof(uint32_t) * bh * (((size_t)L.nqb * L.nkb + soc::kSelGatherChunk - 1) / soc::kSelGatherChunk), 256);
+  off = round_up(off + sizeof(uint32_t) * bh * L.nqb, 256);
   L.pick = off;
   off = round_up(off + sizeof(int64_t) * bh * 4, 256);
   L.cand = off;
   off = round_up(off + d8 * bh * L.nqb * L.nkb, 256);
+  L.cpos = off;
+  off = round_up(off + sizeof(int32_t) * bh * L.nqb * L.nkb, 256);
+  L.wmask = off;  // the mask, when the caller takes none (the fused call)
+  off = round_up(off + bh * L.nqb * L.nkb, 256);
   L.total = off;
   return L;
 }
@@ -728,9 +731,9 @@ int select_setup(const attn_shape_t* shape, const void* q, attn_strides_t q_stri
   a.keep_radius = keep_radius;
   a.tau_mean = tau_mean;
   a.tau_radius = tau_radius;
-  a.mask = block_mask;
-  a.list = block_list;
   char* ws = static_cast<char*>(workspace);
+  a.mask = block_mask ? block_mask : reinterpret_cast<uint8_t*>(ws + L.wmask);
+  a.list = block_list;
   a.qmean = reinterpret_cast<double*>(ws + L.qmean);
   a.cent = reinterpret_cast<double*>(ws + L.cT);
   a.rad2 = reinterpret_cast<double*>(ws + L.rad2);
@@ -742,6 +745,8 @@ int select_setup(const attn_shape_t* shape, const void* q, attn_strides_t q_stri
   a.ccount = reinterpret_cast<uint32_t*>(ws + L.ccount);
   a.pick = reinterpret_cast<int64_t*>(ws + L.pick);
   a.cand = reinterpret_cast<double*>(ws + L.cand);
+  a.cpos = reinterpret_cast<int32_t*>(ws + L.cpos);
+  a.score_wgs = 2 * device_cus();  // the score kernel's LDS and registers allow two per CU
   *out = a;
   return ATTN_OK;
 }
@@ -802,10 +807,7 @@ int attn_block_sparse_prefill(const attn_shape_t* shape, const void* q, attn_str
   a.n_qb = sa.nqb;
   a.mask_stride = sa.nkb;
   a.list_stride = 1 + sa.nkb;
-  a.sel_score = sa.score;
-  a.sel_rad2 = sa.rad2;
-  a.sel_tau_mean = tau_mean;
-  a.sel_tau_radius = tau_radius;
+  a.block_mask = sa.mask;  // the selection's mask (the caller's, or the workspace's)
   e = shape->dtype == ATTN_BF16 ? soc::launch_prefill_bf16(a, stream) : soc::launch_prefill_f32(a, stream);
   return finish(e, stream, "attn_block_sparse_prefill prefill launch");
 }

@@ -86,16 +86,10 @@ __global__ void __launch_bounds__(64) prefill_f32_kernel(AttnArgs a) {
       const int j0 = max(lo, kb * a.block_size), j1 = min(pos, kb * a.block_size + a.block_size - 1);
       if (j0 <= j1) st.run(q, kp, vp, a.kv_st, j0, j1, a.scale_log2);
     }
-  } else if (SPARSE) {  // block mask, or the block selection's scores: the key blocks of the row's range kept
-    const int64_t qrow = ((int64_t)(b * a.Hq + h) * a.n_qb + r / a.block_size) * a.mask_stride;
-    const uint8_t* mrow = a.block_mask ? a.block_mask + qrow : nullptr;
-    const double* srow = a.sel_score ? a.sel_score + qrow : nullptr;
-    const double* rrow = a.sel_score ? a.sel_rad2 + (int64_t)(b * a.Hkv + kvh) * a.mask_stride : nullptr;
-    const double t1 = a.sel_score ? a.sel_tau_mean[b * a.Hq + h] : 0.0;
-    const double t2 = a.sel_score ? a.sel_tau_radius[b * a.Hkv + kvh] : 0.0;
+  } else if (SPARSE) {  // block mask: the kept key blocks of the row's range
+    const uint8_t* mrow = a.block_mask + ((int64_t)(b * a.Hq + h) * a.n_qb + r / a.block_size) * a.mask_stride;
     for (int kb = lo / a.block_size; kb <= pos / a.block_size; ++kb) {
-      const bool kept = mrow ? mrow[kb] != 0 : (srow[kb] > SOC_NEG_INF && (srow[kb] > t1 || rrow[kb] > t2));
-      if (!kept) continue;
+      if (!mrow[kb]) continue;
       const int j0 = max(lo, kb * a.block_size), j1 = min(pos, kb * a.block_size + a.block_size - 1);
       st.run(q, kp, vp, a.kv_st, j0, j1, a.scale_log2);
     }
@@ -146,7 +140,7 @@ template <int D>
 hipError_t launch_prefill_f32_d(const AttnArgs& a, hipStream_t s) {
   const int64_t total = (int64_t)a.B * a.Hq * a.tq;
   const unsigned grid = (unsigned)((total + 63) / 64);
-  if (a.block_list || a.block_mask || a.sel_score)
+  if (a.block_list || a.block_mask)
     hipLaunchKernelGGL((prefill_f32_kernel<D, true>), dim3(grid), dim3(64), 0, s, a);
   else
     hipLaunchKernelGGL((prefill_f32_kernel<D, false>), dim3(grid), dim3(64), 0, s, a);

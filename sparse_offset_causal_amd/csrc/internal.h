@@ -27,12 +27,6 @@ struct AttnArgs {
   const int32_t* block_list;  // device [B, Hq, n_qb, list_stride] or null
   const uint8_t* block_mask;  // device [B, Hq, n_qb, mask_stride] or null
   int32_t block_size, n_qb, list_stride, mask_stride;
-  // block-sparse prefill fused with block selection: the kept blocks are decided from the
-  // selection's scores [B, Hq, n_qb, mask_stride], radii [B, Hkv, mask_stride] and thresholds
-  const double* sel_score;
-  const double* sel_rad2;
-  const double* sel_tau_mean;    // [B, Hq]
-  const double* sel_tau_radius;  // [B, Hkv]
   // split-KV decode
   float* part;     // workspace: partial sums, [B*Hq*tq][nsplit][d] floats, then [..][nsplit][2]
   int32_t nsplit;  // splits per sequence (capacity)
@@ -61,11 +55,18 @@ __host__ __device__ inline size_t decode_rows(const AttnArgs& a) { return (size_
 __host__ __device__ inline size_t decode_o_floats(const AttnArgs& a) { return decode_rows(a) * a.nsplit * a.d; }
 __host__ __device__ inline size_t decode_ml_floats(const AttnArgs& a) { return decode_rows(a) * a.nsplit * 2; }
 
-// Buckets of the per-head score histogram that narrows the order statistic, and the side of
-// the square tile of (query block, key block) scores one workgroup computes.
+// Buckets of the per-head score histogram that narrows the order statistic; the side of the
+// square tile of (query block, key block) scores one MFMA pass covers; the key tiles of one
+// work item of the histogram pass (whose rows stay in one head).
 constexpr int kSelBuckets = 4096;
 constexpr int kScoreTile = 64;
-constexpr int kSelGatherChunk = 8192;  // scores one candidate-gather workgroup scans
+constexpr int kScoreKC = 2;
+// Items per head of the histogram pass: 64-row tiles of the head's query blocks times key
+// chunks of kScoreKC 64-block tiles.
+__host__ __device__ inline int64_t sel_items_per_head(int nqb, int nkb) {
+  return (int64_t)((nqb + kScoreTile - 1) / kScoreTile) *
+         (((nkb + kScoreTile - 1) / kScoreTile + kScoreKC - 1) / kScoreKC);
+}
 
 struct SelectArgs {
   const void* q;
@@ -83,14 +84,16 @@ struct SelectArgs {
   double* qmean;       // workspace [B, Hq, nqb, d]
   double* cent;        // workspace [B, Hkv, nkb, d]  key-block centroids
   double* rad2;        // workspace [B, Hkv, nkb]
-  double* score;       // workspace [B, Hq, nqb, nkb]
+  double* score;       // workspace [B, Hq, nqb, nkb]  (heads scored in one pass)
   double* norm2;       // workspace [B, Hq, nqb] |qmean|^2 then [B, Hkv, nkb] |c|^2
   double* nmax;        // workspace [B*Hq] max |qmean|^2 per head, then [B*Hkv] max |c|^2
-  uint32_t* hpart;     // workspace [B, Hq, score tiles, kSelBuckets / 2]  per-tile histograms (u16 pairs)
-  uint32_t* tflag;     // workspace [B, Hq, score tiles]  1 if the tile holds an admissible pair
-  uint32_t* ccount;    // workspace [B, Hq, gather chunks]  candidates gathered per chunk
+  uint32_t* hpart;     // workspace [B, Hq, items, kSelBuckets / 2]  per-item histograms (u16 pairs)
+  uint32_t* tflag;     // workspace [B, Hq, items]  1 if the item holds an admissible pair
+  uint32_t* ccount;    // workspace [B, Hq, nqb]  candidates of the order statistic per row
   int64_t* pick;       // workspace [B, Hq, 4]  (N, n, bucket, rank within bucket)
-  double* cand;        // workspace [B, Hq, nqb * nkb]  candidates of the order statistic
+  double* cand;        // workspace [B, Hq, nqb, nkb]  candidate values, a segment per row
+  int32_t* cpos;       // workspace [B, Hq, nqb, nkb]  their key blocks
+  int32_t score_wgs;   // persistent workgroups of the score kernel (two per CU)
 };
 
 // One decode step's K/V rows into a W-slot ring cache (slot n_seen[b] % W) and the

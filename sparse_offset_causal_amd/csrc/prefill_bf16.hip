@@ -103,7 +103,7 @@ __device__ __forceinline__ void map_block(int bid, const AttnArgs& a, int n_rg, 
 // rows of one head (measured 1 % faster that way, the window 2 % slower); block-sparse mode
 // stacks rows only (its lists differ by head and are per 128-row block).
 __host__ __device__ inline int heads_per_workgroup(const AttnArgs& a) {
-  if (a.block_list || a.block_mask || a.sel_score || a.window <= 0) return 1;
+  if (a.block_list || a.block_mask || a.window <= 0) return 1;
   return (a.g & 3) == 0 ? 4 : (a.g & 1) == 0 ? 2 : 1;
 }
 
@@ -113,17 +113,16 @@ __device__ __forceinline__ int v_off(int row, int chunk) { return row * D + ((ch
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Which key blocks a workgroup walks: all in its range, those of a kept-block list, those a
-// block mask marks, or those the block selection's scores keep (s1 > tau_mean or rad2 >
-// tau_radius, decided here from the selection's fp64 scores, radii and thresholds).
-enum SparseMode { kDense = 0, kList = 1, kMask = 2, kScore = 3 };
+// Which key blocks a workgroup walks: all in its range, those of a kept-block list, or those a
+// block mask marks.
+enum SparseMode { kDense = 0, kList = 1, kMask = 2 };
 
 constexpr int KBITS = 64;  // chunks of 64 key blocks whose kept sets a workgroup caches in LDS
 
 template <int MODE, bool HSTACK>
 __global__ void __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2)))
 prefill_bf16_d128(AttnArgs a) {
-  __shared__ uint64_t kbits[(MODE == kMask || MODE == kScore) ? KBITS : 1];
+  __shared__ uint64_t kbits[MODE == kMask ? KBITS : 1];
   __shared__ __attribute__((aligned(1024))) bf16_t lds[2 * BUF_ELEMS];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -164,23 +163,10 @@ prefill_bf16_d128(AttnArgs a) {
   // marked) 128-key block, restricted to [t_lo, t_hi) (a contiguous run, in ascending order).
   const int32_t* lst = nullptr;
   const uint8_t* mrow = nullptr;
-  const double* srow = nullptr;  // kScore: s1 of this (b, h, query block) and rad2 of its KV head
-  const double* rrow = nullptr;
-  double tau1 = 0.0, tau2 = 0.0;
-  if (MODE == kScore) {
-    srow = a.sel_score + ((int64_t)(b * a.Hq + h) * a.n_qb + rg) * a.mask_stride;
-    rrow = a.sel_rad2 + (int64_t)(b * a.Hkv + kvh) * a.mask_stride;
-    tau1 = a.sel_tau_mean[b * a.Hq + h];
-    tau2 = a.sel_tau_radius[b * a.Hkv + kvh];
-  }
-  auto kept_block = [&](int kb) __attribute__((always_inline)) -> bool {
-    if (MODE == kMask) return mrow[kb] != 0;
-    const double sv = srow[kb];
-    return sv > SOC_NEG_INF && (sv > tau1 || rrow[kb] > tau2);
-  };
+  auto kept_block = [&](int kb) __attribute__((always_inline)) -> bool { return mrow[kb] != 0; };
   int n0 = 0, n1 = 0;
   const int kb_lo = t_lo >> 1, kb_hi = (t_hi - 1) >> 1;  // key blocks holding tiles of the range
-  // Mask (or score) rows are read 64 key blocks at a time: lane j reads block c + j (blocks
+  // Mask rows are read 64 key blocks at a time: lane j reads block c + j (blocks
   // outside [kb_lo, kb_hi] count as not kept) and a ballot gives the wave-uniform set.
   auto mask_bits = [&](int c) __attribute__((always_inline)) -> uint64_t {
     const int kb = c + lane;
@@ -195,8 +181,8 @@ prefill_bf16_d128(AttnArgs a) {
     int e = n0;
     while (e < n1 && 2 * lst[1 + (e >> 1)] + (e & 1) < t_hi) ++e;
     n1 = e;
-  } else if (MODE == kMask || MODE == kScore) {
-    if (MODE == kMask) mrow = a.block_mask + ((int64_t)(b * a.Hq + h) * a.n_qb + rg) * a.mask_stride;
+  } else if (MODE == kMask) {
+    mrow = a.block_mask + ((int64_t)(b * a.Hq + h) * a.n_qb + rg) * a.mask_stride;
     if (t_lo < t_hi) {
       // The kept sets of the first KBITS chunks of 64 blocks go to LDS once per workgroup (its
       // waves share one (b, h, query block) row here), each wave taking every fourth chunk.
@@ -229,7 +215,7 @@ prefill_bf16_d128(AttnArgs a) {
   bool modd = false;
   auto tile_of = [&](int n) __attribute__((always_inline)) -> int {
     if (MODE == kDense) return t_lo + n;
-    if (MODE == kMask || MODE == kScore) {  // the next tile of the sequence (tiles are asked for in order)
+    if (MODE == kMask) {  // the next tile of the sequence (tiles are asked for in order)
       for (;;) {
         if (modd) {
           modd = false;
@@ -469,8 +455,6 @@ hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((prefill_bf16_d128<kList, false>), dim3((unsigned)grid), dim3(NTHR), 0, s, a);
   else if (a.block_mask)
     hipLaunchKernelGGL((prefill_bf16_d128<kMask, false>), dim3((unsigned)grid), dim3(NTHR), 0, s, a);
-  else if (a.sel_score)
-    hipLaunchKernelGGL((prefill_bf16_d128<kScore, false>), dim3((unsigned)grid), dim3(NTHR), 0, s, a);
   else if (gs > 1)
     hipLaunchKernelGGL((prefill_bf16_d128<kDense, true>), dim3((unsigned)grid), dim3(NTHR), 0, s, a);
   else
