@@ -204,6 +204,62 @@ __device__ bool block_mean(const T* base, int64_t st, int r0, int r1, double* re
   return r1 - r0 <= RB * RG;
 }
 
+// block_mean for a full block of bf16 rows with D = 128 (RB * RG = 128 rows, the usual block
+// size): no row guards, and the loads are buffer loads with the row offset u * RG in the
+// scalar operand (no per-row address arithmetic).  The wave's 4 row groups are combined by a
+// reduce-scatter of lane swaps (columns 0..3 and 4..7 of a thread split between the lane
+// halves, then pairs between the rows of 16), each lane ending with the wave's sums of 2
+// columns, stored as one conflict-free 1 KB LDS row per wave; the 4 waves are added in order.
+// Rows stay in `rows` (a full block fits one batch).
+__device__ void block_mean_full128(const bf16_t* base, int64_t st, double* red, double* out_lds, Row8<bf16_t>* rows) {
+  constexpr int D = 128, C = D / 8, RG = NTHR / C;
+  const int c = threadIdx.x % C, rg = threadIdx.x / C, lane = threadIdx.x & 63, j = lane >> 4;
+  const uint64_t bp = (uint64_t)base;
+  const uint64_t bpu = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(bp >> 32)) << 32) |
+                       (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)bp);
+  const uint32_t row_bytes = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(st * 2));
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)bpu, (short)0, (int)(row_bytes * (RB * RG - 1) + D * 2), 0x00020000);
+  const uint32_t voff = (uint32_t)rg * row_bytes + 16u * (uint32_t)c;
+#pragma unroll
+  for (int u = 0; u < RB; ++u) rows[u].w = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, u * RG * row_bytes, 0);
+  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int u = 0; u < RB; ++u) {
+    double x[8];
+    rows[u].widen(x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += x[e];
+  }
+  // x(l) + x(l ^ 32) of a in the lower lane half and of b in the upper (v_permlane32_swap);
+  // the same between even and odd rows of 16 (v_permlane16_swap)
+  auto pair32 = [](double a, double b) __attribute__((always_inline)) {
+    const auto l = __builtin_amdgcn_permlane32_swap(lo32(a), lo32(b), false, false);
+    const auto h = __builtin_amdgcn_permlane32_swap(hi32(a), hi32(b), false, false);
+    return from32(l[0], h[0]) + from32(l[1], h[1]);
+  };
+  auto pair16 = [](double a, double b) __attribute__((always_inline)) {
+    const auto l = __builtin_amdgcn_permlane16_swap(lo32(a), lo32(b), false, false);
+    const auto h = __builtin_amdgcn_permlane16_swap(hi32(a), hi32(b), false, false);
+    return from32(l[0], h[0]) + from32(l[1], h[1]);
+  };
+  double k4[4], k2[2];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) k4[t] = pair32(acc[t], acc[4 + t]);  // columns 4 (j >> 1) + t
+#pragma unroll
+  for (int t = 0; t < 2; ++t) k2[t] = pair16(k4[t], k4[2 + t]);  // columns 4 (j >> 1) + 2 (j & 1) + t
+  f64x2 w2;
+  w2[0] = k2[0];
+  w2[1] = k2[1];
+  *(f64x2*)(red + (threadIdx.x >> 6) * D + 8 * c + 4 * (j >> 1) + 2 * (j & 1)) = w2;
+  __syncthreads();
+  if (threadIdx.x < D) {
+    const double sum = ((red[threadIdx.x] + red[D + threadIdx.x]) + red[2 * D + threadIdx.x]) + red[3 * D + threadIdx.x];
+    out_lds[threadIdx.x] = sum / (double)(RB * RG);
+  }
+  __syncthreads();
+}
+
 // Squared norm of an LDS vector (wave 0 computes it; lane 0 writes it).
 template <int D>
 __device__ __forceinline__ void write_norm2(const double* v, double* dst) {
@@ -225,7 +281,16 @@ __device__ __forceinline__ void qmean_block(const SelectArgs& a, int id, double*
   const int64_t bh = (int64_t)b * a.Hq + h;
   const T* base = (const T*)a.q + b * a.q_sb + h * a.q_sh;
   Row8<T> rows[RB];
-  block_mean<T, D>(base, a.q_st, qb * a.bs, min((qb + 1) * a.bs, a.tq), red, mean, rows);
+  const int r0 = qb * a.bs, r1 = min((qb + 1) * a.bs, a.tq);
+  if constexpr (std::is_same<T, bf16_t>::value && D == 128) {
+    if (r1 - r0 == RB * (NTHR / (D / 8))) {
+      block_mean_full128(base + r0 * a.q_st, a.q_st, red, mean, rows);
+    } else {
+      block_mean<T, D>(base, a.q_st, r0, r1, red, mean, rows);
+    }
+  } else {
+    block_mean<T, D>(base, a.q_st, r0, r1, red, mean, rows);
+  }
   if (threadIdx.x < D) a.qmean[(bh * a.nqb + qb) * D + threadIdx.x] = mean[threadIdx.x];
   if (a.keep_mean >= 0.0) write_norm2<D>(mean, a.norm2 + bh * a.nqb + qb);
 }
@@ -248,7 +313,17 @@ __device__ __forceinline__ void kstats_block(const SelectArgs& a, int id, double
   const T* base = (const T*)a.k + b * a.k_sb + kvh * a.k_sh;
   const int r0 = kb * a.bs, r1 = min((kb + 1) * a.bs, tkb);
   Row8<T> rows[RB];
-  const bool kept = block_mean<T, D>(base, a.k_st, r0, r1, red, cent, rows);
+  bool kept;
+  if constexpr (std::is_same<T, bf16_t>::value && D == 128) {
+    if (r1 - r0 == RB * (NTHR / (D / 8))) {
+      block_mean_full128(base + r0 * a.k_st, a.k_st, red, cent, rows);
+      kept = true;
+    } else {
+      kept = block_mean<T, D>(base, a.k_st, r0, r1, red, cent, rows);
+    }
+  } else {
+    kept = block_mean<T, D>(base, a.k_st, r0, r1, red, cent, rows);
+  }
   if (threadIdx.x < D) crow[threadIdx.x] = cent[threadIdx.x];
   if (a.keep_mean >= 0.0)
     write_norm2<D>(cent, a.norm2 + (int64_t)a.B * a.Hq * a.nqb + ((int64_t)b * a.Hkv + kvh) * a.nkb + kb);
