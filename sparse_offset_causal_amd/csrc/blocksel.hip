@@ -1230,9 +1230,13 @@ __global__ void __launch_bounds__(NTHR) mask_cand_kernel(SelectArgs a) {
   double* cv = a.cand + row * a.nkb;
   int32_t* cp = a.cpos + row * a.nkb;
   unsigned nc = 0;  // the row's candidates so far
+  // The mask bytes go out as one 8-byte store per lane (lane l: blocks 8l .. 8l + 7 of the
+  // 512-block chunk, from the kept ballots) when the rows are 8-byte aligned.
+  const bool vec = (a.nkb & 7) == 0 && ((uintptr_t)a.mask & 7) == 0;  // (uniform)
   constexpr int MB = 8;  // groups of 64 key blocks whose loads are in flight together
   for (int k0 = 0; k0 < a.nkb; k0 += 64 * MB) {
     double sv[MB], rr[MB];
+    uint64_t kbal[MB];
 #pragma unroll
     for (int u = 0; u < MB; ++u) {
       const int kb = k0 + 64 * u + lane;
@@ -1255,7 +1259,8 @@ __global__ void __launch_bounds__(NTHR) mask_cand_kernel(SelectArgs a) {
         }
         kept = kept || rr[u] > t2;
       }
-      if (kb < a.nkb) mrow[kb] = kept ? 1 : 0;
+      kbal[u] = __ballot(kept);
+      if (!vec && kb < a.nkb) mrow[kb] = kept ? 1 : 0;
       const uint64_t bal = __ballot(cand);
       if (cand) {
         const unsigned o = nc + (unsigned)__popcll(bal & ((1ull << lane) - 1ull));
@@ -1264,32 +1269,18 @@ __global__ void __launch_bounds__(NTHR) mask_cand_kernel(SelectArgs a) {
       }
       nc += (unsigned)__popcll(bal);
     }
+    if (vec && k0 + 8 * lane < a.nkb) {
+      uint64_t w = kbal[0];
+#pragma unroll
+      for (int u = 1; u < MB; ++u) w = (lane >> 3) == u ? kbal[u] : w;
+      const unsigned bits = (unsigned)(w >> (8 * (lane & 7))) & 0xffu;
+      uint64_t by = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) by |= (uint64_t)((bits >> i) & 1u) << (8 * i);
+      *(uint64_t*)(mrow + k0 + 8 * lane) = by;
+    }
   }
   if (lane == 0) a.ccount[row] = nc;
-}
-
-// Compacts one row of keep flags (kb = 0..n_kb-1) into list[0] = count, list[1..] = kb.
-// Called by all 256 threads of the block with the same row.
-template <typename KeepFn>
-__device__ void compact_row(int n_kb, KeepFn keep, uint8_t* mask_row, int32_t* list_row, int* wsum) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int base = 0;
-  for (int k0 = 0; k0 < n_kb; k0 += NTHR) {
-    const int kb = k0 + threadIdx.x;
-    const bool kept = kb < n_kb && keep(kb);
-    if (mask_row && kb < n_kb) mask_row[kb] = kept ? 1 : 0;
-    const unsigned long long bal = __ballot(kept);
-    const int before = __popcll(bal & ((1ull << lane) - 1ull));
-    if (lane == 0) wsum[wave] = __popcll(bal);
-    __syncthreads();
-    int wbase = base;
-    for (int w = 0; w < wave; ++w) wbase += wsum[w];
-    if (kept && list_row) list_row[1 + wbase + before] = kb;
-    const int total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-    __syncthreads();
-    base += total;
-  }
-  if (threadIdx.x == 0 && list_row) list_row[0] = base;
 }
 
 // One wave per (b, h, query block) row: the mask bytes and the ascending kept list, 64 key
@@ -1335,11 +1326,45 @@ __global__ void __launch_bounds__(NTHR) mask_kernel(SelectArgs a) {
   if (lane == 0 && lrow) lrow[0] = base;
 }
 
-__global__ void __launch_bounds__(NTHR) list_from_mask_kernel(int32_t n_kb, const uint8_t* mask, int32_t* list) {
-  __shared__ int wsum[4];
-  const int64_t row = blockIdx.x;
+// Kept lists from a byte mask: list[0] = the row's count, list[1..] = its kept key blocks in
+// ascending order.  One wave per row; lane l takes the 8 consecutive blocks 8l .. 8l + 7 of
+// each 512-block chunk (one 8-byte load when the rows are 8-byte aligned), and a wave prefix
+// sum of the lanes' counts places each lane's blocks.
+__global__ void __launch_bounds__(NTHR) list_from_mask_kernel(int64_t rows, int32_t n_kb, const uint8_t* mask,
+                                                              int32_t* list) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * (NTHR / 64) + (threadIdx.x >> 6);
+  if (row >= rows) return;
   const uint8_t* m = mask + row * n_kb;
-  compact_row(n_kb, [&](int kb) { return m[kb] != 0; }, nullptr, list + row * (1 + n_kb), wsum);
+  int32_t* lrow = list + row * (1 + (int64_t)n_kb);
+  const bool vec = (n_kb & 7) == 0 && ((uintptr_t)mask & 7) == 0;  // (uniform)
+  int base = 0;
+  for (int k0 = 0; k0 < n_kb; k0 += 512) {
+    const int kb0 = k0 + 8 * lane;
+    unsigned bits = 0;  // bit i: block kb0 + i is kept
+    if (vec) {
+      const uint64_t by = kb0 < n_kb ? *(const uint64_t*)(m + kb0) : 0ull;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) bits |= ((by >> (8 * i)) & 0xffu) ? 1u << i : 0u;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) bits |= (kb0 + i < n_kb && m[kb0 + i] != 0) ? 1u << i : 0u;
+    }
+    const int c = __popc(bits);
+    int incl = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
+    }
+    int at = 1 + base + incl - c;
+    while (bits) {
+      lrow[at++] = kb0 + __builtin_ctz(bits);
+      bits &= bits - 1;
+    }
+    base += __builtin_amdgcn_readlane(incl, 63);
+  }
+  if (lane == 0) lrow[0] = base;
 }
 
 template <typename T, int D>
@@ -1373,7 +1398,9 @@ hipError_t launch_select_d(const SelectArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(pick_kernel, dim3((unsigned)(bh + nrad)), dim3(PICK_THR), 0, s, a);
     hipLaunchKernelGGL(mask_cand_kernel, dim3((gq + NTHR / 64 - 1) / (NTHR / 64)), dim3(NTHR), 0, s, a);
     hipLaunchKernelGGL(threshold_kernel, dim3((unsigned)bh), dim3(1024), 0, s, a);
-    if (a.list) hipLaunchKernelGGL(list_from_mask_kernel, dim3(gq), dim3(NTHR), 0, s, a.nkb, a.mask, a.list);
+    if (a.list)
+      hipLaunchKernelGGL(list_from_mask_kernel, dim3((gq + NTHR / 64 - 1) / (NTHR / 64)), dim3(NTHR), 0, s, (int64_t)gq,
+                         a.nkb, a.mask, a.list);
   }
   return hipGetLastError();
 }
@@ -1398,7 +1425,8 @@ hipError_t launch_block_select(const SelectArgs& a, bool in_bf16, hipStream_t s)
 
 hipError_t launch_list_from_mask(int64_t rows, int32_t n_kb, const uint8_t* mask, int32_t* list, hipStream_t s) {
   if (rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(list_from_mask_kernel, dim3((unsigned)rows), dim3(NTHR), 0, s, n_kb, mask, list);
+  hipLaunchKernelGGL(list_from_mask_kernel, dim3((unsigned)((rows + NTHR / 64 - 1) / (NTHR / 64))), dim3(NTHR), 0, s, rows,
+                     n_kb, mask, list);
   return hipGetLastError();
 }
 

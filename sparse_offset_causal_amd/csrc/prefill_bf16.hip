@@ -43,7 +43,8 @@
 // is a multiple of 8, each XCD is given whole KV groups (their K/V stay in that XCD's L2);
 // within an XCD the workgroups of one KV group are dispatched together (all its query
 // tiles and heads, the query tiles with the most keys first), so they stream the group's
-// K/V tiles at about the same time.
+// K/V tiles at about the same time.  With per-sequence cache offsets (up to 64 sequences)
+// the KV groups are taken in descending order of their sequence's cached length.
 
 #include <type_traits>
 
@@ -67,6 +68,21 @@ typedef short s16x8 __attribute__((__vector_size__(16)));
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 typedef __attribute__((address_space(3))) s16x4* lds_s16x4_ptr;
 
+// The sequence of descending-length rank r (0 = the most cached keys; equal offsets in
+// sequence order) among the batch's B <= 64 sequences, from the cache offsets: lane i counts
+// the sequences ranked before sequence i, and the lane whose count is r names it.  One wave.
+__device__ __forceinline__ int seq_of_rank(const AttnArgs& a, int r) {
+  const int lane = threadIdx.x & 63;
+  const int my = lane < a.B ? a.cache_off[lane] : 0;  // lanes past B are never read or chosen
+  int before = 0;
+  for (int j = 0; j < a.B; ++j) {
+    const int oj = __builtin_amdgcn_readlane(my, j);
+    before += (oj > my) | ((oj == my) & (j < lane));
+  }
+  const unsigned long long hit = __builtin_amdgcn_ballot_w64(lane < a.B && before == r);
+  return __ffsll(hit) - 1;
+}
+
 // Workgroup -> (row group rg, first query head hq of its head group, sequence b).  A
 // workgroup takes gs query heads of one KV group (gs divides g) over rwg = 128 / gs rows.
 __device__ __forceinline__ void map_block(int bid, const AttnArgs& a, int n_rg, int gs, int& rg, int& hq, int& b) {
@@ -74,15 +90,18 @@ __device__ __forceinline__ void map_block(int bid, const AttnArgs& a, int n_rg, 
   const int units = a.B * a.Hkv;
   if ((units & 7) == 0) {
     // unit-major within the XCD: all row groups and heads of one KV group run together, so
-    // the group's K/V stream is fetched from HBM about once and re-read from L2
+    // the group's K/V stream is fetched from HBM about once and re-read from L2.  With
+    // per-sequence cache offsets (a batch of chunks at different cache lengths) the units are
+    // taken longest sequence first, so the grid does not end on a long sequence's tiles.
     const int xcd = bid & 7, j = bid >> 3;
     const int per_unit = n_rg * hgn;
     const int ul = j / per_unit;
     const int rem = j - ul * per_unit;
     const int rg_rev = rem / hgn, hgi = rem - rg_rev * hgn;
     const int unit = ul * 8 + xcd;
-    b = unit / a.Hkv;
-    const int kvh = unit - b * a.Hkv;
+    const int br = unit / a.Hkv;
+    const int kvh = unit - br * a.Hkv;
+    b = (a.cache_off && a.B > 1 && a.B <= 64) ? seq_of_rank(a, br) : br;
     hq = kvh * a.g + hgi * gs;
     rg = n_rg - 1 - rg_rev;
   } else {

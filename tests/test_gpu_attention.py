@@ -79,6 +79,10 @@ PREFILL_CASES = [
     (2, 4, 2, 333, 900, [100, 567], 150, True),
     (1, 12, 2, 200, 500, [300], 64, True),
     (1, 6, 2, 250, 250, None, 40, False),
+    # chunks at different cache lengths on the KV-group-per-XCD grid: the groups run longest
+    # sequence first (equal offsets, and a full 64-sequence batch)
+    (8, 4, 1, 130, 700, [570, 3, 300, 129, 64, 570, 0, 411], 0, True),
+    (64, 2, 1, 16, 200, [(37 * i) % 185 for i in range(64)], 0, False),
 ]
 
 

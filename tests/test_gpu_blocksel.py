@@ -140,6 +140,7 @@ def test_block_sparse_prefill_on_selected_blocks():
     # B, Hq, Hkv, Tq, Tk, offsets, window, sink, keeps
     (1, 8, 2, 2048, 2048, None, 0, False, (0.1, 0.125)),       # planted-outlier prompt, one shot
     (3, 8, 2, 300, 1500, [1200, 37, 640], 0, True, (0.1, 0.1)),  # query-chunked: chunks at cache offsets
+    (4, 8, 2, 256, 1200, [900, 37, 640, 400], 0, True, (0.1, 0.1)),  # the same, KV groups longest first
     (2, 16, 4, 384, 1400, [1000, 500], 700, True, (0.2, 0.05)),  # chunks with a window
 ])
 def test_fused_block_sparse_prefill(case):
