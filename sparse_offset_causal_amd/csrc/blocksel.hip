@@ -222,7 +222,7 @@ __device__ void block_mean_full128(const bf16_t* base, int64_t st, double* red, 
       __builtin_amdgcn_make_buffer_rsrc((void*)bpu, (short)0, (int)(row_bytes * (RB * RG - 1) + D * 2), 0x00020000);
   const uint32_t voff = (uint32_t)rg * row_bytes + 16u * (uint32_t)c;
 #pragma unroll
-  for (int u = 0; u < RB; ++u) rows[u].w = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, u * RG * row_bytes, 0);
+  for (int u = 0; u < RB; ++u) rows[u].w = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, u * RG * row_bytes, kLoadReadOnce);
   double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
   for (int u = 0; u < RB; ++u) {

@@ -294,7 +294,7 @@ decode_split_bf16_d128(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void_ptr)(vstage(stage_tag) + wofs + i * 512), 16, v_lane,
-                                               blk_off + 4 * i * row_bytes, 0, 0);
+                                               blk_off + 4 * i * row_bytes, 0, kLoadReadOnce);
   };
 
   // query row of this lane: rho = head-in-group * tq + r

@@ -16,6 +16,12 @@ typedef uint32_t u32x2 __attribute__((__vector_size__(8)));
 
 #define SOC_NEG_INF (-__builtin_inff())
 
+// Cache policy operand of a buffer load for data read once per call (the nt bit of gfx950's
+// cache policy): whole lines a wave reads in one instruction and never asks for again.  It is
+// not used where a wave reads part of a line and relies on the cache for the rest of it (the
+// MFMA-layout K loads of decode), nor where other workgroups re-read the same tiles (prefill).
+constexpr int kLoadReadOnce = 2;
+
 // Raw hardware 2^x (v_exp_f32).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

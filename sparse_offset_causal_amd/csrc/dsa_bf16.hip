@@ -874,7 +874,8 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) ds
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void_ptr)(vstage(stage_tag) + i * 512), 16,
-                                               (uint32_t)ent[n * KB + 4 * i + vr] * row_bytes + v_sw, 0, 0, 0);
+                                               (uint32_t)ent[n * KB + 4 * i + vr] * row_bytes + v_sw, 0, 0,
+                                               kLoadReadOnce);
   };
   // Every step issues one block (past the last block it issues the last block again, into a
   // stage already consumed), so exactly NST - 1 blocks are younger than the one a step

@@ -185,7 +185,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) m
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         stg[BUF][i] = __builtin_amdgcn_raw_buffer_load_b128(crs, (uint32_t)(4 * wave + i) * crow + (uint32_t)(16 * lane),
-                                                            k0 * crow, 0);
+                                                            k0 * crow, kLoadReadOnce);
       // every lane loads (lanes 32..63 the same bytes as lanes 0..31, one request per line), so
       // a block is always WAVE_LOADS loads and the compiler can count them
       stg[BUF][4] = __builtin_amdgcn_raw_buffer_load_b128(rrs, rope_v, k0 * rrow, 0);
