@@ -83,6 +83,8 @@ PREFILL_CASES = [
     # sequence first (equal offsets, and a full 64-sequence batch)
     (8, 4, 1, 130, 700, [570, 3, 300, 129, 64, 570, 0, 411], 0, True),
     (64, 2, 1, 16, 200, [(37 * i) % 185 for i in range(64)], 0, False),
+    # 65 sequences: past the ranked order's one-wave limit the groups keep sequence order
+    (65, 8, 8, 3, 90, [(29 * i) % 88 for i in range(65)], 0, True),
 ]
 
 
