@@ -400,6 +400,18 @@ def bench_block_sparse(steps, warmup, T=65536, BS=128):
     n = 64
     rp["cpu_baseline"] = OracleClock.run([lambda i=i: unit(i) for i in range(n)], [unit_work(i) for i in range(n)], 1e12,
                                          "TFLOP/s", "(head, 128-row query block) pieces of the block-sparse prefill")
+    # the selection per KV group (its query heads and its key head, every row): thresholds are per
+    # head and per KV head, so each group's selection is the workload's own
+    from oracle import select_blocks
+    hkv = k.shape[1]
+    g = q.shape[1] // hkv
+
+    def sel_unit(kv):
+        select_blocks(w.q[:, g * kv:g * (kv + 1)], w.k[:, kv:kv + 1], BS, keep_mean=w.keep_mean,
+                      keep_radius=w.keep_radius)
+
+    rs["cpu_baseline"] = OracleClock.run([lambda kv=kv: sel_unit(kv) for kv in range(hkv)], [sel_bytes / hkv] * hkv, 1e9,
+                                         "GB/s", f"KV groups ({g} query heads and their key head, all {T} rows) of the selection")
     return rs, rp
 
 
