@@ -449,17 +449,26 @@ prefill_bf16_d128(AttnArgs a) {
 
   const float lt = pair_sum(l_run);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  if (my_row < a.tq) {
-    bf16_t* op = (bf16_t*)a.o + b * a.o_sb + h * a.o_sh + (int64_t)my_row * a.o_st;
+  // The output tile goes out through LDS (free once the loop's last barrier has passed): each
+  // wave writes its 32 rows x 128 columns into its own 8 KB, 16-byte chunk c of row r at chunk
+  // c ^ (r & 15), then stores whole rows, four per instruction (lane j: row 4i + j / 16, chunk
+  // j % 16), instead of 8 bytes of 32 different rows per instruction.
+  bf16_t* ot = lds + wave * (32 * D);
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
+  for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        bf16x4 w;
+    for (int g4 = 0; g4 < 4; ++g4) {
+      bf16x4 w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (bf16_t)(oacc[tb][4 * g4 + e] * inv);
-        *(bf16x4*)(op + tb * 32 + 8 * g4 + 4 * hh) = w;
-      }
+      for (int e = 0; e < 4; ++e) w[e] = (bf16_t)(oacc[tb][4 * g4 + e] * inv);
+      *(bf16x4*)(ot + l32 * D + (((4 * tb + g4) ^ (l32 & 15)) << 3) + 4 * hh) = w;
+    }
+  bf16_t* ob = (bf16_t*)a.o + b * a.o_sb + h * a.o_sh;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int rr = 4 * i + (lane >> 4), ch = lane & 15;
+    const u32x4 x = *(const u32x4*)(ot + rr * D + ((ch ^ (rr & 15)) << 3));
+    if (wr0 + rr < a.tq) *(u32x4*)(ob + (int64_t)(wr0 + rr) * a.o_st + 8 * ch) = x;
   }
 }
 
