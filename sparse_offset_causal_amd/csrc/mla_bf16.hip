@@ -306,14 +306,27 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) m
     // the row's sum over the 4 lanes that share it
     l_run += __shfl_xor(l_run, 16, 64);
     l_run += __shfl_xor(l_run, 32, 64);
-    if (row_ok) {
+    if (row_ok && wave == 0 && G == 0) {
       const int64_t prow = ((int64_t)b * R + rho) * a.nsplit + s;
-      float* po = a.part_o + prow * MR + 128 * wave;  // this wave's dims 128 wave + 16 w + 4 G + v
+      a.part_ml[2 * prow] = m_run;
+      a.part_ml[2 * prow + 1] = l_run;
+    }
+    // The partial latent output goes out through LDS: each wave's 16 rows x 128 dims (dims
+    // 128 wave + 16 w + 4 G + v in lane (i16, G)) into its own 8 KB, 16-byte chunk c of row r
+    // at chunk c ^ r, then stored as whole 512-byte row slices, two rows per instruction,
+    // instead of 64 bytes of each of 16 rows per instruction.  The barrier: every wave is done
+    // with the last block's stage.
+    __syncthreads();
+    float* ost = reinterpret_cast<float*>(lds) + wave * (16 * 128);
 #pragma unroll
-      for (int w = 0; w < 8; ++w) *(f32x4*)(po + 16 * w + 4 * G) = oacc[w];
-      if (wave == 0 && G == 0) {
-        a.part_ml[2 * prow] = m_run;
-        a.part_ml[2 * prow + 1] = l_run;
+    for (int w = 0; w < 8; ++w) *(f32x4*)(ost + i16 * 128 + (((4 * w + G) ^ i16) << 2)) = oacc[w];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = 2 * i + (lane >> 5), cc = lane & 31;
+      const f32x4 x = *(const f32x4*)(ost + r * 128 + ((cc ^ r) << 2));
+      if (rg * 16 + r < R) {
+        const int64_t prow = ((int64_t)b * R + rg * 16 + r) * a.nsplit + s;
+        *(f32x4*)(a.part_o + prow * MR + 128 * wave + 4 * cc) = x;
       }
     }
   }  // work loop
