@@ -291,12 +291,29 @@ prefill_bf16_d128(AttnArgs a) {
   int t_next = n0 < n1 ? tile_of(n0) : 0;
   if (n0 < n1) issue_tile(t_next, 0);
 
-  bf16x8 qf[8];
+  // The wave's 32 query rows go HBM -> LDS by DMA too, into its own 8 KB of the second buffer
+  // (free until the first tile step fills it): whole rows, four per instruction, 16-byte chunk c
+  // of row r at chunk c ^ (r & 15); rows at or beyond tq fall outside the buffer range and read
+  // as zero.  They are read into registers in the MFMA operand layout before the loop.
+  const uint32_t q_row_bytes = (uint32_t)a.q_st * 2u;
+  bf16_t* qlds = lds + BUF_ELEMS + wave * (32 * D);
+  {
+    // (base and range made visibly uniform: a descriptor the compiler takes for divergent is
+    // applied lane group by lane group)
+    const int nq = __builtin_amdgcn_readfirstlane(max(0, min(32, a.tq - wr0)));
+    const uint64_t qb = (uint64_t)(qp + (int64_t)wr0 * a.q_st);
+    const uint64_t qbu = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(qb >> 32)) << 32) |
+                         (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)qb);
+    const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)qbu, (short)0, __builtin_amdgcn_readfirstlane((int)(nq * q_row_bytes)), 0x00020000);
+    const int qr = lane >> 4;
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    u32x4 z = {0u, 0u, 0u, 0u};
-    qf[ks] = (my_row < a.tq) ? *(const bf16x8*)(qp + (int64_t)my_row * a.q_st + 16 * ks + 8 * hh) : as_bf16x8(z);
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (lds_void_ptr)(qlds + i * 512), 16,
+                                               qr * q_row_bytes + (uint32_t)(((lane & 15) ^ ((4 * i + qr) & 15)) << 4),
+                                               (uint32_t)(4 * i) * q_row_bytes, 0, 0);
   }
+  bf16x8 qf[8];
 
   f32x16 oacc[4];
 #pragma unroll
@@ -441,6 +458,10 @@ prefill_bf16_d128(AttnArgs a) {
   };
 
   wait_vmem();
+  __syncthreads();
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) qf[ks] = *(const bf16x8*)(qlds + l32 * D + (((2 * ks + hh) ^ (l32 & 15)) << 3));
+  // every wave has its query fragments before the first tile step's DMA refills the buffer
   __syncthreads();
   for (int n = n0; n < n1; n += 2) {
     tile_step(n, std::integral_constant<int, 0>{});
