@@ -186,7 +186,6 @@ __global__ void __launch_bounds__(64 * IDX_WAVES) __attribute__((amdgpu_waves_pe
   __syncthreads();
 
   const int nhb = A.Hi / 16;
-  const int qper = A.Hi * (DI / 8);  // 16-byte query pieces per row
   const uint32_t row_bytes = (uint32_t)A.ki_st * 2u;
   for (int g = lo, phase = 0; g < hi; ++phase) {
     // The phase's row segments (unused ones empty, with u0 past every block).

@@ -291,13 +291,15 @@ prefill_bf16_d128(AttnArgs a) {
   int t_next = n0 < n1 ? tile_of(n0) : 0;
   if (n0 < n1) issue_tile(t_next, 0);
 
-  // The wave's 32 query rows go HBM -> LDS by DMA too, into its own 8 KB of the second buffer
-  // (free until the first tile step fills it): whole rows, four per instruction, 16-byte chunk c
-  // of row r at chunk c ^ (r & 15); rows at or beyond tq fall outside the buffer range and read
-  // as zero.  They are read into registers in the MFMA operand layout before the loop.
+  // Dense mode: the wave's 32 query rows go HBM -> LDS by DMA too, into its own 8 KB of the
+  // second buffer (free until the first tile step fills it): whole rows, four per instruction,
+  // 16-byte chunk c of row r at chunk c ^ (r & 15); rows at or beyond tq fall outside the buffer
+  // range and read as zero.  They are read into registers in the MFMA operand layout before the
+  // loop.  The sparse modes, whose workgroups walk few tiles, load them into registers directly
+  // (the LDS route's extra barrier cost them more than its whole-row loads saved).
   const uint32_t q_row_bytes = (uint32_t)a.q_st * 2u;
   bf16_t* qlds = lds + BUF_ELEMS + wave * (32 * D);
-  {
+  if constexpr (MODE == kDense) {
     // (base and range made visibly uniform: a descriptor the compiler takes for divergent is
     // applied lane group by lane group)
     const int nq = __builtin_amdgcn_readfirstlane(max(0, min(32, a.tq - wr0)));
@@ -314,6 +316,13 @@ prefill_bf16_d128(AttnArgs a) {
                                                (uint32_t)(4 * i) * q_row_bytes, 0, 0);
   }
   bf16x8 qf[8];
+  if constexpr (MODE != kDense) {
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      u32x4 z = {0u, 0u, 0u, 0u};
+      qf[ks] = (my_row < a.tq) ? *(const bf16x8*)(qp + (int64_t)my_row * a.q_st + 16 * ks + 8 * hh) : as_bf16x8(z);
+    }
+  }
 
   f32x16 oacc[4];
 #pragma unroll
@@ -459,10 +468,12 @@ prefill_bf16_d128(AttnArgs a) {
 
   wait_vmem();
   __syncthreads();
+  if constexpr (MODE == kDense) {
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) qf[ks] = *(const bf16x8*)(qlds + l32 * D + (((2 * ks + hh) ^ (l32 & 15)) << 3));
-  // every wave has its query fragments before the first tile step's DMA refills the buffer
-  __syncthreads();
+    for (int ks = 0; ks < 8; ++ks) qf[ks] = *(const bf16x8*)(qlds + l32 * D + (((2 * ks + hh) ^ (l32 & 15)) << 3));
+    // every wave has its query fragments before the first tile step's DMA refills the buffer
+    __syncthreads();
+  }
   for (int n = n0; n < n1; n += 2) {
     tile_step(n, std::integral_constant<int, 0>{});
     if (n + 1 < n1) tile_step(n + 1, std::integral_constant<int, 1>{});
